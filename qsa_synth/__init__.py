@@ -1,0 +1,140 @@
+"""Seeded synthetic inputs for the QSA prompt-attention path.
+
+This module only draws random arrays; it holds none of the method's
+arithmetic.  Both the fp64 oracle (``oracle/``) and the HIP path
+(``quantized_sparse_flash_amd``) are fed from here, so their inputs are
+identical bit for bit.
+
+Workload shapes follow the pages (quantized_sparse_flash audits):
+  * 2 KV groups x 12 query heads, head dim 256 ("sol_r6_qsa", experiment
+    contract and delivered change; "opus_r9_qsa", what changed: HPG x QCH);
+  * int8 K/V codes with one fp16 scale per 64 dims (a half4 per cell)
+    ("sol_r6_qsa", delivered change);
+  * deterministic random inputs from rng seed 5 ("sol_r6_qsa", actual runs);
+  * a 2051-cell selection budget ("sol_r6_qsa", delivered change).
+
+The value distributions (queries N(0,1) as fp16, codes uniform in
+[-127, 127], scales uniform in [0.002, 0.02], selection scores N(0,1) fp32)
+are this build's stated recipe: the pages name the kinds of inputs but not
+their distributions.
+
+Generator: numpy PCG64 seeded with the tuple (seed, T, pos0, layer); draws
+happen in a fixed order (q, kq, ksc, vq, vsc, scores) so that adding the
+optional score draw never changes the other arrays.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+N_GROUPS = 2
+HEADS_PER_GROUP = 12
+HEAD_DIM = 256
+SCALE_BLOCK = 64
+BUDGET = 2051
+CHUNK = 64
+SEED = 5
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """One layer's synthetic inputs (host numpy arrays)."""
+
+    T: int
+    pos0: int
+    budget: int
+    n_cells: int
+    q: np.ndarray            # [T][G*HPG][D] float16
+    kq: np.ndarray           # [G][n_cells][D] int8
+    ksc: np.ndarray          # [G][n_cells][D/64] float16
+    vq: np.ndarray           # [G][n_cells][D] int8
+    vsc: np.ndarray          # [G][n_cells][D/64] float16
+    scores: Optional[np.ndarray]  # [T][G][n_cells] float32, or None
+
+    @property
+    def n_groups(self) -> int:
+        return self.kq.shape[0]
+
+    @property
+    def heads_per_group(self) -> int:
+        return self.q.shape[1] // self.kq.shape[0]
+
+    @property
+    def head_dim(self) -> int:
+        return self.q.shape[2]
+
+
+def layer_inputs(T: int, pos0: int, layer: int = 0, seed: int = SEED, *,
+                 budget: int = BUDGET, n_cells: Optional[int] = None,
+                 n_groups: int = N_GROUPS, heads_per_group: int = HEADS_PER_GROUP,
+                 head_dim: int = HEAD_DIM, with_scores: Optional[bool] = None,
+                 code_max: int = 127, scale_lo: float = 0.002,
+                 scale_hi: float = 0.02) -> LayerInputs:
+    """Draw one layer's inputs.
+
+    ``n_cells`` defaults to ``pos0 + T`` (the KV history holds every cell a
+    token of this prompt chunk can see).  Scores are drawn when some token
+    is above budget (``pos0 + T > budget``) unless ``with_scores`` forces it.
+    """
+    if n_cells is None:
+        n_cells = pos0 + T
+    if n_cells < pos0 + T:
+        raise ValueError("n_cells must cover pos0 + T")
+    if with_scores is None:
+        with_scores = pos0 + T > budget
+    rng = np.random.default_rng([seed, T, pos0, layer])
+    H = n_groups * heads_per_group
+    nb = head_dim // SCALE_BLOCK
+    q = rng.standard_normal((T, H, head_dim), dtype=np.float32).astype(np.float16)
+    kq = rng.integers(-code_max, code_max + 1, (n_groups, n_cells, head_dim), dtype=np.int8)
+    ksc = rng.uniform(scale_lo, scale_hi, (n_groups, n_cells, nb)).astype(np.float16)
+    vq = rng.integers(-code_max, code_max + 1, (n_groups, n_cells, head_dim), dtype=np.int8)
+    vsc = rng.uniform(scale_lo, scale_hi, (n_groups, n_cells, nb)).astype(np.float16)
+    scores = None
+    if with_scores:
+        scores = rng.standard_normal((T, n_groups, n_cells), dtype=np.float32)
+    return LayerInputs(T=T, pos0=pos0, budget=budget, n_cells=n_cells, q=q, kq=kq,
+                       ksc=ksc, vq=vq, vsc=vsc, scores=scores)
+
+
+def score_rows(T: int, n_groups: int, n_cells: int, seed: int, *, kind: str = "normal",
+               levels: int = 4) -> np.ndarray:
+    """Selection-score arrays for top-k tests.
+
+    kind:
+      "normal"    N(0,1) fp32 (the workload's scores);
+      "quantized" N(0,1) rounded to ``levels`` distinct values (many ties);
+      "signed_zero"  a mix of +0.0, -0.0 and a few N(0,1) values.
+    """
+    rng = np.random.default_rng([seed, T, n_cells, 17])
+    s = rng.standard_normal((T, n_groups, n_cells), dtype=np.float32)
+    if kind == "normal":
+        return s
+    if kind == "quantized":
+        return np.floor(s * (levels / 4.0)).astype(np.float32)
+    if kind == "signed_zero":
+        sign = rng.integers(0, 2, s.shape).astype(bool)
+        z = np.where(sign, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        keep = rng.random(s.shape) < 0.05
+        return np.where(keep, s, z).astype(np.float32)
+    raise ValueError(kind)
+
+
+# Named workloads (sizes of the pages' measured configurations).
+WORKLOADS = {
+    # tiny prompt under budget: token t sees cells 0..t; one layer
+    "t96_pos0": dict(T=96, pos0=0, layers=1),
+    # 12 back-to-back layers at pos0 0 (identity selection)
+    "t512_pos0_x12": dict(T=512, pos0=0, layers=12),
+    "t1024_pos0_x12": dict(T=1024, pos0=0, layers=12),
+    "t1984_pos0_x12": dict(T=1984, pos0=0, layers=12),
+    # chunks that cross the 2051-cell budget
+    "t96_pos2050": dict(T=96, pos0=2050, layers=1),
+    "t32_pos2050": dict(T=32, pos0=2050, layers=1),
+    # long context: every token takes its top-2051 of ~32K cells
+    "t1984_pos30000": dict(T=1984, pos0=30000, layers=1),
+    # decode-merge: 4 tokens at position 8192, split into 64-cell chunks
+    "decode4_pos8192": dict(T=4, pos0=8192, layers=1),
+}
