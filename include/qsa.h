@@ -1,0 +1,142 @@
+/*
+ * qsa.h -- C ABI of libqsa, the MI355X (gfx950) QSA prompt-attention path.
+ *
+ * QSA attention, as the quantized_sparse_flash audit pages describe it: every
+ * prompt token t of a chunk that starts at absolute position pos0 sees the
+ * n_kv(t) = pos0 + t + 1 KV cells [0, n_kv(t)) of each KV group.  For each
+ * (token, group) row the path
+ *   1. selects cells: all of them when n_kv(t) <= budget ("identity ids"),
+ *      otherwise the `budget` cells with the largest selection score
+ *      (page "round 6 track b - qsa flash", delivered change; ties to the
+ *      lower index, ids ascending -- the reading this library takes);
+ *   2. gathers the selected cells' int8 K/V codes and their fp16 scales, one
+ *      per 64 dims (same page, delivered change: four scales per cell);
+ *   3. computes S = 0.0625 * Q K^T for the group's 12 query heads chunk by
+ *      chunk over 64 selected cells with an online softmax, forms P in fp16
+ *      and accumulates P V (page "opus_r9_qsa", what changed);
+ *   4. optionally writes per-chunk partials (o, m, l) that are combined by a
+ *      log-sum-exp merge (page "round 27 track b - qsa prep and merge",
+ *      decision and correctness: head stride 258, chunk stride 6192).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device (HBM) pointers owned by the caller;
+ *     the library keeps no reference after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; results are visible after the caller
+ *     synchronises the stream.  Calls are thread-safe.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     non-zero return means nothing was enqueued, except QSA_ERR_LAUNCH,
+ *     which reports a failed kernel launch.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Element layouts are dense and row-major with the shapes given below;
+ *     all counts are in elements.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QSA_OK 0
+#define QSA_ERR_ARG (-1)         /* NULL or misaligned pointer, bad struct */
+#define QSA_ERR_UNSUPPORTED (-2) /* heads_per_group != 12, head_dim != 256, budget too large */
+#define QSA_ERR_SHAPE (-3)       /* T < 1, pos0 < 0, n_groups < 1, n_cells < pos0 + T, ... */
+#define QSA_ERR_LAUNCH (-4)      /* the HIP runtime rejected a kernel launch */
+
+/* Library limits. */
+#define QSA_HEADS_PER_GROUP 12 /* query heads that share one KV group */
+#define QSA_HEAD_DIM 256       /* dims per head; scales cover 64 dims each */
+#define QSA_SCALE_BLOCK 64     /* dims per fp16 scale */
+#define QSA_CHUNK 64           /* selected cells per chunk / partial record */
+#define QSA_PART_STRIDE 258    /* floats per partial record: o[256], m, l */
+#define QSA_MAX_BUDGET 65536   /* largest supported budget */
+#define QSA_DEFAULT_BUDGET 2051
+
+/* Shape of one prompt chunk of one layer. */
+typedef struct {
+  int32_t T;               /* query tokens in the chunk, >= 1 */
+  int32_t pos0;            /* absolute position of token 0, >= 0 */
+  int32_t n_groups;        /* KV groups G, >= 1 (the pages use 2) */
+  int32_t heads_per_group; /* must be QSA_HEADS_PER_GROUP */
+  int32_t head_dim;        /* must be QSA_HEAD_DIM */
+  int32_t budget;          /* selection budget B, 1..QSA_MAX_BUDGET */
+  int64_t n_cells;         /* KV cells held per group (>= pos0 + T); also the
+                              row stride of `scores` */
+} qsa_shape;
+
+/*
+ * qsa_topk -- step 1: selected ids of every (token, group) row.
+ *
+ *   scores : device, const float [T][G][n_cells]; row (t, g) is read only at
+ *            cells [0, n_kv(t)) and only when n_kv(t) > budget.  May be NULL
+ *            when pos0 + T <= budget (no row above budget).  Scores must not
+ *            be NaN (NaN rows give an unspecified but in-range selection);
+ *            -0.0 and +0.0 are equal.
+ *   ids    : device, int32 [T][G][budget], written in full:
+ *            n_kv(t) <= budget: 0, 1, ..., n_kv(t)-1, then -1 padding;
+ *            n_kv(t) >  budget: the budget cells of largest score (equal
+ *            scores: lower index first), in ascending order.
+ * Alignment: 4 bytes.  Results are bit-exact (integer output).
+ */
+int qsa_topk(const qsa_shape *shape, const float *scores, int32_t *ids, void *stream);
+
+/*
+ * qsa_flash -- steps 2-4: attention over the selected cells.
+ *
+ *   q        : device, fp16 [T][G*12][256]; head h belongs to group h / 12.
+ *   kq, vq   : device, int8 [G][n_cells][256] K and V codes.
+ *   ksc, vsc : device, fp16 [G][n_cells][4]; dim d of cell c is scaled by
+ *              ksc[g][c][d / 64] (resp. vsc).
+ *   ids      : device, int32 [T][G][budget] as written by qsa_topk.  Read
+ *              only for rows with n_kv(t) > budget; rows under budget use
+ *              the identity cells whatever ids holds.  May be NULL when
+ *              pos0 + T <= budget.  Each id read must lie in [0, n_kv(t));
+ *              an id outside it is clamped into [0, n_cells) (the output is
+ *              then unspecified, the kernel never reads out of bounds).
+ *   out      : device, fp16 [T][G*12][256], the softmax-weighted values,
+ *              rounded to nearest even.  Written in fused mode (part == NULL);
+ *              not touched in split mode.
+ *   part     : NULL for fused mode.  Otherwise split mode: device, float
+ *              [T][ceil(budget/64)][G*12][258]; for token t and chunk
+ *              k < ceil(n_sel(t)/64), n_sel(t) = min(n_kv(t), budget), the
+ *              record at ((t*KC + k)*G*12 + h)*258 holds o[0..255] (the
+ *              unnormalised sum of exp(s_c - m) v_c over the chunk's cells),
+ *              m (the chunk's max of s_c, natural-log units) and l (the sum of
+ *              exp(s_c - m)).  Records of chunks a token does not have are not
+ *              written.
+ * Alignment: 16 bytes for q, kq, vq, out and part; 8 for ksc, vsc; 4 for ids.
+ * Numerics: fp16 MFMA products with fp32 accumulation; relative L2 error
+ * against exact attention about 4e-4 on the pages' value ranges.
+ */
+int qsa_flash(const qsa_shape *shape, const _Float16 *q, const int8_t *kq, const _Float16 *ksc,
+              const int8_t *vq, const _Float16 *vsc, const int32_t *ids, _Float16 *out,
+              float *part, void *stream);
+
+/*
+ * qsa_merge -- log-sum-exp merge of split-mode partials (page "round 27
+ * track b - qsa prep and merge", decision: the (m, l) merge of chunk
+ * partials).  For token t the first ceil(n_sel(t)/64) records of each head
+ * are merged:  M = max m_k,  L = sum l_k e^(m_k - M),
+ *              out = fp16( sum e^(m_k - M) o_k / L ).
+ *   part : device, float [T][ceil(budget/64)][G*12][258] (qsa_flash layout).
+ *   out  : device, fp16 [T][G*12][256].
+ * Alignment: 16 bytes for both.
+ */
+int qsa_merge(const qsa_shape *shape, const float *part, _Float16 *out, void *stream);
+
+/* Human-readable text of a status code (static storage). */
+const char *qsa_status_string(int status);
+
+/* Floats needed by a split-mode `part` buffer for this shape (0 on a bad
+ * shape); a host-only helper. */
+int64_t qsa_part_elems(const qsa_shape *shape);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

@@ -1,0 +1,183 @@
+"""quantized_sparse_flash_amd -- the QSA prompt-attention path on MI355X.
+
+A thin ctypes binding over ``libqsa.so`` (C ABI in ``include/qsa.h``).  The
+functions carry the C names and only marshal arguments: shapes, dtypes and
+devices are checked, device pointers and the current HIP stream are passed
+through, and every step of the path runs in the library's gfx950 kernels.
+PyTorch supplies device memory and streams.  There is no CPU fallback: if
+the library is missing or cannot be loaded, calls raise.
+
+Entry points (all asynchronous on the current stream):
+  qsa_topk(shape, scores, ids)                                 selection
+  qsa_flash(shape, q, kq, ksc, vq, vsc, ids, out, part=None)   attention
+  qsa_merge(shape, part, out)                                  LSE merge
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libqsa.so")
+
+QSA_OK = 0
+QSA_ERR_ARG = -1
+QSA_ERR_UNSUPPORTED = -2
+QSA_ERR_SHAPE = -3
+QSA_ERR_LAUNCH = -4
+HEADS_PER_GROUP = 12
+HEAD_DIM = 256
+CHUNK = 64
+PART_STRIDE = 258
+DEFAULT_BUDGET = 2051
+MAX_BUDGET = 65536
+
+EXPORTED = ("qsa_topk", "qsa_flash", "qsa_merge", "qsa_status_string", "qsa_part_elems")
+
+
+class QsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s (status %d)" % (where, qsa_status_string(status), status))
+        self.status = status
+
+
+class _CShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("pos0", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("heads_per_group", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("budget", ctypes.c_int32), ("n_cells", ctypes.c_int64)]
+
+
+@dataclasses.dataclass
+class QsaShape:
+    """Mirror of the C ``qsa_shape``; ``n_cells`` defaults to pos0 + T."""
+
+    T: int
+    pos0: int
+    n_groups: int = 2
+    budget: int = DEFAULT_BUDGET
+    n_cells: Optional[int] = None
+    heads_per_group: int = HEADS_PER_GROUP
+    head_dim: int = HEAD_DIM
+
+    def __post_init__(self):
+        if self.n_cells is None:
+            self.n_cells = self.pos0 + self.T
+
+    @property
+    def n_heads(self) -> int:
+        return self.n_groups * self.heads_per_group
+
+    @property
+    def n_part_chunks(self) -> int:
+        return -(-self.budget // CHUNK)
+
+    def c(self) -> _CShape:
+        return _CShape(self.T, self.pos0, self.n_groups, self.heads_per_group, self.head_dim,
+                       self.budget, self.n_cells)
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libqsa.so (raises if it is absent: build it with
+    ``python -m quantized_sparse_flash_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libqsa.so not built (%s); run `python -m "
+                           "quantized_sparse_flash_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    SP = ctypes.POINTER(_CShape)
+    lib.qsa_topk.argtypes = [SP, P, P, P]
+    lib.qsa_flash.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+    lib.qsa_merge.argtypes = [SP, P, P, P]
+    lib.qsa_status_string.argtypes = [ctypes.c_int]
+    lib.qsa_status_string.restype = ctypes.c_char_p
+    lib.qsa_part_elems.argtypes = [SP]
+    lib.qsa_part_elems.restype = ctypes.c_int64
+    for f in (lib.qsa_topk, lib.qsa_flash, lib.qsa_merge):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def qsa_status_string(status: int) -> str:
+    return load_library().qsa_status_string(int(status)).decode()
+
+
+def qsa_part_elems(shape: QsaShape) -> int:
+    cs = shape.c()
+    return int(load_library().qsa_part_elems(ctypes.byref(cs)))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name, dtype, shape=None):
+    """Device pointer of a contiguous CUDA tensor of the given dtype/shape."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def qsa_topk(shape: QsaShape, scores, ids, stream=None) -> None:
+    """Write selected ids [T][G][budget] (int32) for every (token, group)."""
+    import torch
+    s = shape
+    sc = _dev_ptr(scores, "scores", torch.float32, (s.T, s.n_groups, s.n_cells))
+    ip = _dev_ptr(ids, "ids", torch.int32, (s.T, s.n_groups, s.budget))
+    cs = s.c()
+    rc = load_library().qsa_topk(ctypes.byref(cs), sc, ip, _stream(stream))
+    if rc != QSA_OK:
+        raise QsaError(rc, "qsa_topk")
+
+
+def qsa_flash(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None, stream=None) -> None:
+    """Attention over the selected cells: fused (writes ``out``) or, with
+    ``part``, split mode (writes per-chunk (o, m, l) records)."""
+    import torch
+    s = shape
+    H, D, N, G = s.n_heads, s.head_dim, s.n_cells, s.n_groups
+    nb = D // 64
+    args = [_dev_ptr(q, "q", torch.float16, (s.T, H, D)),
+            _dev_ptr(kq, "kq", torch.int8, (G, N, D)),
+            _dev_ptr(ksc, "ksc", torch.float16, (G, N, nb)),
+            _dev_ptr(vq, "vq", torch.int8, (G, N, D)),
+            _dev_ptr(vsc, "vsc", torch.float16, (G, N, nb)),
+            _dev_ptr(ids, "ids", torch.int32, (s.T, G, s.budget)),
+            _dev_ptr(out, "out", torch.float16, (s.T, H, D)),
+            _dev_ptr(part, "part", torch.float32, (s.T, s.n_part_chunks, H, PART_STRIDE))]
+    cs = s.c()
+    rc = load_library().qsa_flash(ctypes.byref(cs), *args, _stream(stream))
+    if rc != QSA_OK:
+        raise QsaError(rc, "qsa_flash")
+
+
+def qsa_merge(shape: QsaShape, part, out, stream=None) -> None:
+    """Log-sum-exp merge of split-mode records into ``out`` [T][H][D] fp16."""
+    import torch
+    s = shape
+    H = s.n_heads
+    pp = _dev_ptr(part, "part", torch.float32, (s.T, s.n_part_chunks, H, PART_STRIDE))
+    op = _dev_ptr(out, "out", torch.float16, (s.T, H, s.head_dim))
+    cs = s.c()
+    rc = load_library().qsa_merge(ctypes.byref(cs), pp, op, _stream(stream))
+    if rc != QSA_OK:
+        raise QsaError(rc, "qsa_merge")

@@ -1,0 +1,111 @@
+// qsa_api.hip -- the C ABI of libqsa (declared in include/qsa.h).
+//
+// Every entry point validates its arguments on the host, before anything is
+// enqueued, then launches the gfx950 kernels on the caller's stream.  The
+// library allocates nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qsa.h"
+#include "qsa_launch.h"
+
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks shared by all entry points.  Returns QSA_OK or an error.
+int check_shape(const qsa_shape* s) {
+  if (!s) return QSA_ERR_ARG;
+  if (s->heads_per_group != QSA_HEADS_PER_GROUP || s->head_dim != QSA_HEAD_DIM)
+    return QSA_ERR_UNSUPPORTED;
+  if (s->budget < 1 || s->budget > QSA_MAX_BUDGET) return QSA_ERR_UNSUPPORTED;
+  if (s->T < 1 || s->pos0 < 0 || s->n_groups < 1) return QSA_ERR_SHAPE;
+  if (s->n_cells < (int64_t)s->pos0 + s->T) return QSA_ERR_SHAPE;
+  // cell indices are int32 on the device; grids are 1-D
+  if (s->n_cells > INT32_MAX || (int64_t)s->pos0 + s->T > INT32_MAX) return QSA_ERR_SHAPE;
+  const int64_t rows = (int64_t)s->T * s->n_groups;
+  const int64_t kc = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
+  if (rows > INT32_MAX / 4 || rows * kc > INT32_MAX / 4) return QSA_ERR_SHAPE;
+  if ((int64_t)s->n_groups * QSA_HEADS_PER_GROUP * s->T > INT32_MAX / 4) return QSA_ERR_SHAPE;
+  return QSA_OK;
+}
+
+bool any_above_budget(const qsa_shape* s) { return (int64_t)s->pos0 + s->T > s->budget; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qsa_status_string(int status) {
+  switch (status) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_ARG: return "invalid argument (NULL or misaligned pointer)";
+    case QSA_ERR_UNSUPPORTED: return "unsupported configuration (heads_per_group, head_dim or budget)";
+    case QSA_ERR_SHAPE: return "invalid shape (T, pos0, n_groups or n_cells)";
+    case QSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t qsa_part_elems(const qsa_shape* s) {
+  if (check_shape(s) != QSA_OK) return 0;
+  const int64_t kc = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
+  return (int64_t)s->T * kc * s->n_groups * QSA_HEADS_PER_GROUP * QSA_PART_STRIDE;
+}
+
+int qsa_topk(const qsa_shape* s, const float* scores, int32_t* ids, void* stream) {
+  int rc = check_shape(s);
+  if (rc != QSA_OK) return rc;
+  if (!ids || !aligned(ids, 4)) return QSA_ERR_ARG;
+  if (any_above_budget(s) && (!scores || !aligned(scores, 4))) return QSA_ERR_ARG;
+  return launch_status(qsa::launch_topk(scores, ids, s->T, s->pos0, s->n_groups, s->budget,
+                                        s->n_cells, (hipStream_t)stream));
+}
+
+int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
+              const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+              float* part, void* stream) {
+  int rc = check_shape(s);
+  if (rc != QSA_OK) return rc;
+  if (!q || !kq || !ksc || !vq || !vsc) return QSA_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(kq, 16) || !aligned(vq, 16) || !aligned(ksc, 8) ||
+      !aligned(vsc, 8))
+    return QSA_ERR_ARG;
+  if (any_above_budget(s) && (!ids || !aligned(ids, 4))) return QSA_ERR_ARG;
+  const bool split = part != nullptr;
+  if (split) {
+    if (!aligned(part, 16)) return QSA_ERR_ARG;
+  } else {
+    if (!out || !aligned(out, 16)) return QSA_ERR_ARG;
+  }
+  qsa::RowArgs a;
+  a.q = q;
+  a.kq = kq;
+  a.ksc = ksc;
+  a.vq = vq;
+  a.vsc = vsc;
+  a.ids = ids;
+  a.out = out;
+  a.part = part;
+  a.T = s->T;
+  a.pos0 = s->pos0;
+  a.G = s->n_groups;
+  a.budget = s->budget;
+  a.KC = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
+  a.n_items = 0;
+  a.n_cells = s->n_cells;
+  return launch_status(qsa::launch_flash_rows(a, split, (hipStream_t)stream));
+}
+
+int qsa_merge(const qsa_shape* s, const float* part, _Float16* out, void* stream) {
+  int rc = check_shape(s);
+  if (rc != QSA_OK) return rc;
+  if (!part || !out || !aligned(part, 16) || !aligned(out, 16)) return QSA_ERR_ARG;
+  return launch_status(qsa::launch_merge(part, out, s->T, s->n_groups * QSA_HEADS_PER_GROUP,
+                                         s->pos0, s->budget, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+// qsa_launch.h -- host-side launchers of the QSA kernels (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// Arguments of the attention kernels (pointers are device pointers).
+struct RowArgs {
+  const _Float16* q;
+  const int8_t* kq;
+  const _Float16* ksc;
+  const int8_t* vq;
+  const _Float16* vsc;
+  const int32_t* ids;
+  _Float16* out;
+  float* part;
+  int T, pos0, G, budget, KC, n_items;
+  int64_t n_cells;
+};
+
+hipError_t launch_topk(const float* scores, int32_t* ids, int T, int pos0, int G, int budget,
+                       int64_t n_cells, hipStream_t stream);
+hipError_t launch_merge(const float* part, _Float16* out, int T, int H, int pos0, int budget,
+                        hipStream_t stream);
+hipError_t launch_flash_rows(const RowArgs& a, bool split, hipStream_t stream);
+
+}  // namespace qsa

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports what include/qsa.h declares, rejects bad
+arguments before launching anything, and its constants match the pages.
+No compute call is made: every call here fails validation on the host."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import quantized_sparse_flash_amd as qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_constants.json")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+
+
+def _header_defines():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(QSA_\w+)\s+\(?(-?\d+)\)?", text)}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qsa.load_library()
+    declared = _declared_functions()
+    assert set(declared) == set(qsa.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_pages_and_binding():
+    d = _header_defines()
+    g = json.load(open(GOLDEN))
+    assert d["QSA_HEADS_PER_GROUP"] == g["heads_per_group"]["value"] == qsa.HEADS_PER_GROUP
+    assert d["QSA_HEAD_DIM"] == g["head_dim"]["value"] == qsa.HEAD_DIM
+    assert d["QSA_CHUNK"] == g["chunk"]["value"] == qsa.CHUNK
+    assert d["QSA_DEFAULT_BUDGET"] == g["budget"]["value"] == qsa.DEFAULT_BUDGET
+    assert d["QSA_PART_STRIDE"] == g["part_head_stride"]["value"] == qsa.PART_STRIDE
+    assert d["QSA_HEAD_DIM"] // d["QSA_SCALE_BLOCK"] == g["scales_per_cell"]["value"]
+    # chunk stride of the partial records: 24 heads x 258 floats
+    n_heads = g["n_groups"]["value"] * g["heads_per_group"]["value"]
+    assert n_heads * d["QSA_PART_STRIDE"] == g["part_chunk_stride"]["value"]
+    for k in ("QSA_OK", "QSA_ERR_ARG", "QSA_ERR_UNSUPPORTED", "QSA_ERR_SHAPE", "QSA_ERR_LAUNCH"):
+        assert getattr(qsa, k) == d[k]
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert qsa.qsa_status_string(code)
+    assert qsa.qsa_status_string(-99) == "unknown status"
+
+
+def test_part_elems_layout():
+    s = qsa.QsaShape(T=4, pos0=8192)
+    assert qsa.qsa_part_elems(s) == 4 * 33 * 24 * 258
+    assert qsa.qsa_part_elems(qsa.QsaShape(T=0, pos0=0)) == 0
+
+
+def _raw(lib, fn, shape, *ptrs):
+    cs = shape.c()
+    return getattr(lib, fn)(ctypes.byref(cs), *[ctypes.c_void_p(p) if p else None for p in ptrs])
+
+
+@pytest.mark.parametrize("shape,expect", [
+    (dict(T=0, pos0=0), qsa.QSA_ERR_SHAPE),
+    (dict(T=4, pos0=-1), qsa.QSA_ERR_SHAPE),
+    (dict(T=4, pos0=0, n_groups=0), qsa.QSA_ERR_SHAPE),
+    (dict(T=4, pos0=10, n_cells=13), qsa.QSA_ERR_SHAPE),
+    (dict(T=4, pos0=0, heads_per_group=8), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(T=4, pos0=0, head_dim=128), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(T=4, pos0=0, budget=0), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(T=4, pos0=0, budget=qsa.MAX_BUDGET + 1), qsa.QSA_ERR_UNSUPPORTED),
+])
+def test_bad_shapes_are_rejected(shape, expect):
+    lib = qsa.load_library()
+    s = qsa.QsaShape(**shape)
+    fake = 0x10000  # never dereferenced: validation fails first
+    assert _raw(lib, "qsa_flash", s, fake, fake, fake, fake, fake, fake, fake, None, None) == expect
+    assert _raw(lib, "qsa_topk", s, fake, fake, None) == expect
+    assert _raw(lib, "qsa_merge", s, fake, fake, None) == expect
+
+
+def test_null_and_misaligned_pointers_are_rejected():
+    lib = qsa.load_library()
+    A = 0x10000
+    under = qsa.QsaShape(T=8, pos0=0)
+    over = qsa.QsaShape(T=8, pos0=2050)
+    E = qsa.QSA_ERR_ARG
+    # q, kq, ksc, vq, vsc, ids, out, part
+    assert _raw(lib, "qsa_flash", under, 0, A, A, A, A, 0, A, 0, None) == E
+    assert _raw(lib, "qsa_flash", under, A + 8, A, A, A, A, 0, A, 0, None) == E   # q 16 B
+    assert _raw(lib, "qsa_flash", under, A, A, A + 4, A, A, 0, A, 0, None) == E   # ksc 8 B
+    assert _raw(lib, "qsa_flash", under, A, A, A, A, A, 0, 0, 0, None) == E       # no out
+    assert _raw(lib, "qsa_flash", over, A, A, A, A, A, 0, A, 0, None) == E        # ids needed
+    assert _raw(lib, "qsa_flash", over, A, A, A, A, A, A + 2, A, 0, None) == E    # ids 4 B
+    assert _raw(lib, "qsa_flash", under, A, A, A, A, A, 0, 0, A + 8, None) == E   # part 16 B
+    assert _raw(lib, "qsa_topk", over, 0, A, None) == E                           # scores
+    assert _raw(lib, "qsa_topk", under, 0, 0, None) == E                          # ids
+    assert _raw(lib, "qsa_merge", under, A, A + 2, None) == E
+    assert _raw(lib, "qsa_merge", under, 0, A, None) == E

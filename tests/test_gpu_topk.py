@@ -1,0 +1,68 @@
+"""GPU qsa_topk against the oracle's selection: ids must match bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+import qsa_synth
+from gpu_util import gpu_topk, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs_with_scores(T, pos0, budget, kind, seed, n_cells=None):
+    inp = qsa_synth.layer_inputs(T, pos0, seed=seed, budget=budget, n_cells=n_cells,
+                                 with_scores=True)
+    if kind != "normal":
+        inp.scores = qsa_synth.score_rows(T, 2, inp.n_cells, seed, kind=kind, levels=4)
+    return inp
+
+
+@pytest.mark.parametrize("T,pos0,budget,kind", [
+    (96, 2050, 2051, "normal"), (32, 2050, 2051, "normal"), (4, 2049, 2051, "normal"),
+    (64, 1987, 2051, "normal"), (200, 1900, 2051, "normal"),
+    (40, 60, 5, "normal"), (40, 60, 5, "quantized"), (30, 3000, 2051, "quantized"),
+    (16, 700, 300, "signed_zero"), (8, 100, 1, "normal"), (8, 5000, 4096, "normal"),
+])
+def test_topk_matches_oracle(T, pos0, budget, kind):
+    inp = _inputs_with_scores(T, pos0, budget, kind, seed=T + pos0)
+    ref = oracle.select(T, pos0, budget, inp.scores, 2, inp.n_cells)
+    np.testing.assert_array_equal(gpu_topk(inp), ref)
+
+
+def test_topk_all_equal_and_monotone_rows():
+    T, pos0, B = 4, 3000, 2051
+    inp = _inputs_with_scores(T, pos0, B, "normal", seed=2)
+    N = inp.n_cells
+    for s in (np.zeros((T, 2, N), np.float32),
+              -np.tile(np.arange(N, dtype=np.float32), (T, 2, 1)),
+              np.tile(np.arange(N, dtype=np.float32), (T, 2, 1))):
+        inp.scores = s
+        np.testing.assert_array_equal(gpu_topk(inp), oracle.select(T, pos0, B, s, 2, N))
+
+
+def test_topk_scores_row_stride_is_n_cells():
+    # n_cells larger than pos0 + T: rows are n_cells apart, cells past n_kv
+    # (filled with +inf here) are never selected
+    T, pos0, B = 6, 2100, 2051
+    inp = _inputs_with_scores(T, pos0, B, "normal", seed=9, n_cells=pos0 + T + 37)
+    for t in range(T):
+        inp.scores[t, :, pos0 + t + 1:] = np.inf
+    np.testing.assert_array_equal(gpu_topk(inp),
+                                  oracle.select(T, pos0, B, inp.scores, 2, inp.n_cells))
+
+
+def test_topk_long_context_sampled_rows():
+    # T=1984 at pos0 30000 over 31,984 cells (the long-context workload):
+    # full GPU selection, every row checked for validity, sampled rows
+    # checked bit-exactly
+    inp = qsa_synth.layer_inputs(1984, 30000)
+    dev = upload(inp)
+    ids = gpu_topk(inp, dev)
+    assert ids.shape == (1984, 2, 2051)
+    assert np.all(ids >= 0)
+    assert np.all(np.diff(ids, axis=2) > 0)                      # strictly ascending
+    assert np.all(ids[:, :, -1] <= 30000 + np.arange(1984)[:, None])
+    rng = np.random.default_rng(3)
+    for t in sorted(set([0, 1983] + rng.integers(0, 1984, 14).tolist())):
+        ref = oracle.select(1, 30000 + t, 2051, inp.scores[t:t + 1], 2, inp.n_cells)
+        np.testing.assert_array_equal(ids[t:t + 1], ref)
