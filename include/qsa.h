@@ -20,7 +20,8 @@
  *
  * Conventions for every entry point:
  *   - Pointers marked "device" are device (HBM) pointers owned by the caller;
- *     the library keeps no reference after the call returns.
+ *     the library keeps no reference after the call returns and allocates no
+ *     memory itself (scratch comes in through a workspace argument).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; results are visible after the caller
  *     synchronises the stream.  Calls are thread-safe.
@@ -100,6 +101,11 @@ int qsa_topk(const qsa_shape *shape, const float *scores, int32_t *ids, void *st
  *   out      : device, fp16 [T][G*12][256], the softmax-weighted values,
  *              rounded to nearest even.  Written in fused mode (part == NULL);
  *              not touched in split mode.
+ *   workspace, workspace_bytes : device scratch of at least
+ *              qsa_flash_workspace_bytes(shape) bytes, 256-byte aligned, owned
+ *              by the caller; overwritten by the call, so two calls in flight
+ *              at once must not share it.  May be NULL (with size 0) when
+ *              that size is 0.
  *   part     : NULL for fused mode.  Otherwise split mode: device, float
  *              [T][ceil(budget/64)][G*12][258]; for token t and chunk
  *              k < ceil(n_sel(t)/64), n_sel(t) = min(n_kv(t), budget), the
@@ -108,13 +114,24 @@ int qsa_topk(const qsa_shape *shape, const float *scores, int32_t *ids, void *st
  *              m (the chunk's max of s_c, natural-log units) and l (the sum of
  *              exp(s_c - m)).  Records of chunks a token does not have are not
  *              written.
- * Alignment: 16 bytes for q, kq, vq, out and part; 8 for ksc, vsc; 4 for ids.
+ * Alignment: 16 bytes for q, kq, vq, out and part; 8 for ksc, vsc; 4 for ids;
+ * 256 for workspace.
  * Numerics: fp16 MFMA products with fp32 accumulation; relative L2 error
  * against exact attention about 4e-4 on the pages' value ranges.
  */
 int qsa_flash(const qsa_shape *shape, const _Float16 *q, const int8_t *kq, const _Float16 *ksc,
               const int8_t *vq, const _Float16 *vsc, const int32_t *ids, _Float16 *out,
-              float *part, void *stream);
+              float *part, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace qsa_flash needs for this shape in fused mode
+ * (0 when no token is under budget, and split mode needs none); a host-only
+ * helper.  The fused path dequantises the cells that tokens under budget
+ * share -- cells [0, pos0 + t_id) of every group, t_id being the number of
+ * such tokens -- once per call into this workspace: 64 KB per group and
+ * 64-cell chunk (fp16 K and V^T).
+ */
+int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
 
 /*
  * qsa_merge -- log-sum-exp merge of split-mode partials (page "round 27

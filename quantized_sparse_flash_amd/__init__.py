@@ -34,7 +34,8 @@ PART_STRIDE = 258
 DEFAULT_BUDGET = 2051
 MAX_BUDGET = 65536
 
-EXPORTED = ("qsa_topk", "qsa_flash", "qsa_merge", "qsa_status_string", "qsa_part_elems")
+EXPORTED = ("qsa_topk", "qsa_flash", "qsa_merge", "qsa_status_string", "qsa_part_elems",
+            "qsa_flash_workspace_bytes")
 
 
 class QsaError(RuntimeError):
@@ -94,7 +95,9 @@ def load_library(path: str = LIB_PATH):
     P = ctypes.c_void_p
     SP = ctypes.POINTER(_CShape)
     lib.qsa_topk.argtypes = [SP, P, P, P]
-    lib.qsa_flash.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+    lib.qsa_flash.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]
+    lib.qsa_flash_workspace_bytes.argtypes = [SP]
+    lib.qsa_flash_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_merge.argtypes = [SP, P, P, P]
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
@@ -113,6 +116,30 @@ def qsa_status_string(status: int) -> str:
 def qsa_part_elems(shape: QsaShape) -> int:
     cs = shape.c()
     return int(load_library().qsa_part_elems(ctypes.byref(cs)))
+
+
+def qsa_flash_workspace_bytes(shape: QsaShape) -> int:
+    cs = shape.c()
+    return int(load_library().qsa_flash_workspace_bytes(ctypes.byref(cs)))
+
+
+_ws_cache = {}
+
+
+def flash_workspace(shape: QsaShape, device=None):
+    """A uint8 device tensor large enough for qsa_flash on ``shape`` (kept
+    and reused per device; grows when a larger one is needed), or None."""
+    import torch
+    need = qsa_flash_workspace_bytes(shape)
+    if need == 0:
+        return None
+    dev = torch.device(device if device is not None else "cuda")
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
 
 
 def _stream(stream):
@@ -149,11 +176,21 @@ def qsa_topk(shape: QsaShape, scores, ids, stream=None) -> None:
         raise QsaError(rc, "qsa_topk")
 
 
-def qsa_flash(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None, stream=None) -> None:
+def qsa_flash(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None, workspace=None,
+              stream=None) -> None:
     """Attention over the selected cells: fused (writes ``out``) or, with
-    ``part``, split mode (writes per-chunk (o, m, l) records)."""
+    ``part``, split mode (writes per-chunk (o, m, l) records).  ``workspace``
+    (uint8 device tensor) defaults to a cached one of the needed size; calls
+    in flight on different streams at once must pass their own."""
     import torch
     s = shape
+    if part is None and workspace is None:
+        workspace = flash_workspace(s, q.device)
+    ws_ptr = None
+    ws_bytes = 0
+    if workspace is not None:
+        ws_ptr = _dev_ptr(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
     H, D, N, G = s.n_heads, s.head_dim, s.n_cells, s.n_groups
     nb = D // 64
     args = [_dev_ptr(q, "q", torch.float16, (s.T, H, D)),
@@ -165,7 +202,7 @@ def qsa_flash(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None, stream=
             _dev_ptr(out, "out", torch.float16, (s.T, H, D)),
             _dev_ptr(part, "part", torch.float32, (s.T, s.n_part_chunks, H, PART_STRIDE))]
     cs = s.c()
-    rc = load_library().qsa_flash(ctypes.byref(cs), *args, _stream(stream))
+    rc = load_library().qsa_flash(ctypes.byref(cs), *args, ws_ptr, ws_bytes, _stream(stream))
     if rc != QSA_OK:
         raise QsaError(rc, "qsa_flash")
 

@@ -33,6 +33,12 @@ int check_shape(const qsa_shape* s) {
 
 bool any_above_budget(const qsa_shape* s) { return (int64_t)s->pos0 + s->T > s->budget; }
 
+// Tokens [0, t_id) of the chunk are under budget (identity selection).
+int identity_tokens(const qsa_shape* s) {
+  const int64_t under = (int64_t)s->budget - s->pos0;
+  return (int)(under < 0 ? 0 : (under > s->T ? s->T : under));
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
 
 }  // namespace
@@ -65,9 +71,14 @@ int qsa_topk(const qsa_shape* s, const float* scores, int32_t* ids, void* stream
                                         s->n_cells, (hipStream_t)stream));
 }
 
+int64_t qsa_flash_workspace_bytes(const qsa_shape* s) {
+  if (check_shape(s) != QSA_OK) return 0;
+  return qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+}
+
 int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
               const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
-              float* part, void* stream) {
+              float* part, void* workspace, int64_t workspace_bytes, void* stream) {
   int rc = check_shape(s);
   if (rc != QSA_OK) return rc;
   if (!q || !kq || !ksc || !vq || !vsc) return QSA_ERR_ARG;
@@ -97,7 +108,18 @@ int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Fl
   a.KC = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
   a.n_items = 0;
   a.n_cells = s->n_cells;
-  return launch_status(qsa::launch_flash_rows(a, split, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  if (split) return launch_status(qsa::launch_flash_rows(a, true, 0, st));
+  // fused: tokens under budget (a prefix of the chunk) see a common prefix
+  // of cells, dequantised once into the workspace and shared by the tiled
+  // kernel; tokens above budget gather their own ids row by row
+  const int t_id = identity_tokens(s);
+  const int64_t need = qsa::tile_workspace_bytes(s->n_groups, t_id, s->pos0);
+  if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need))
+    return QSA_ERR_ARG;
+  rc = launch_status(qsa::launch_flash_tile(a, t_id, workspace, st));
+  if (rc != QSA_OK) return rc;
+  return launch_status(qsa::launch_flash_rows(a, false, t_id, st));
 }
 
 int qsa_merge(const qsa_shape* s, const float* part, _Float16* out, void* stream) {

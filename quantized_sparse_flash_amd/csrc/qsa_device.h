@@ -46,11 +46,10 @@ template <int BL, int BH>
 __device__ __forceinline__ uint32_t i8pair_to_h2(uint32_t lo_src, uint32_t hi_src) {
   uint32_t r;
   static_assert(BL >= 0 && BL < 4 && BH >= 0 && BH < 4, "byte select");
-  asm volatile(
-      "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%c3\n\t"
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%c3\n\t"
       "v_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%c4"
       : "=&v"(r)
-      : "v"(lo_src), "v"(hi_src), "i"(BL), "i"(BH));
+      : "v"(lo_src), "v"(hi_src), "i"(BL), "i"(BH));  // pure: no side effects
   return r;
 }
 

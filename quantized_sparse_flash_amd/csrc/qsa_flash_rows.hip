@@ -244,9 +244,12 @@ __global__ __launch_bounds__(256) void flash_rows_kernel(RowArgs a) {
   }
 }
 
-hipError_t launch_flash_rows(const RowArgs& args_in, bool split, hipStream_t stream) {
+hipError_t launch_flash_rows(const RowArgs& args_in, bool split, int t_begin,
+                             hipStream_t stream) {
   RowArgs a = args_in;
-  a.n_items = split ? a.T * a.KC * a.G : a.T * a.G;
+  if (split) t_begin = 0;
+  a.n_items = split ? a.T * a.KC * a.G : (a.T - t_begin) * a.G;
+  if (a.n_items <= 0) return hipSuccess;
   dim3 grid((a.n_items + 3) / 4), block(256);
   if (split)
     flash_rows_kernel<true><<<grid, block, 0, stream>>>(a);

@@ -24,6 +24,13 @@ hipError_t launch_topk(const float* scores, int32_t* ids, int T, int pos0, int G
                        int64_t n_cells, hipStream_t stream);
 hipError_t launch_merge(const float* part, _Float16* out, int T, int H, int pos0, int budget,
                         hipStream_t stream);
-hipError_t launch_flash_rows(const RowArgs& a, bool split, hipStream_t stream);
+// Row kernel: one wavefront per (token, group) row for tokens [t_begin, T)
+// (fused), or per (token, group, chunk) for all tokens (split mode).
+hipError_t launch_flash_rows(const RowArgs& a, bool split, int t_begin, hipStream_t stream);
+// Tile path: fused attention of tokens [0, t_count), all under budget.  It
+// dequantises cells [0, pos0 + t_count) of every group into `ws` (which must
+// hold tile_workspace_bytes(G, t_count, pos0) bytes), then attends.
+int64_t tile_workspace_bytes(int G, int t_count, int pos0);
+hipError_t launch_flash_tile(const RowArgs& a, int t_count, void* ws, hipStream_t stream);
 
 }  // namespace qsa

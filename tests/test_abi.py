@@ -56,15 +56,36 @@ def test_status_strings():
     assert qsa.qsa_status_string(-99) == "unknown status"
 
 
+def test_flash_workspace_size():
+    # fused path: 64 KB per group and 64-cell chunk of the shared prefix
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=1984, pos0=0)) == 2 * 31 * 65536
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == 2 * 33 * 65536
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=30000)) == 0
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=0, pos0=0)) == 0
+
+
+def test_missing_workspace_is_rejected():
+    lib = qsa.load_library()
+    A = 0x10000
+    s = qsa.QsaShape(T=8, pos0=0)
+    E = qsa.QSA_ERR_ARG
+    need = qsa.qsa_flash_workspace_bytes(s)
+    assert _raw(lib, "qsa_flash", s, A, A, A, A, A, 0, A, 0, 0, 0, None) == E
+    assert _raw(lib, "qsa_flash", s, A, A, A, A, A, 0, A, 0, A, need - 1, None) == E
+    assert _raw(lib, "qsa_flash", s, A, A, A, A, A, 0, A, 0, A + 16, need, None) == E
+
+
 def test_part_elems_layout():
     s = qsa.QsaShape(T=4, pos0=8192)
     assert qsa.qsa_part_elems(s) == 4 * 33 * 24 * 258
     assert qsa.qsa_part_elems(qsa.QsaShape(T=0, pos0=0)) == 0
 
 
-def _raw(lib, fn, shape, *ptrs):
+def _raw(lib, fn, shape, *args):
     cs = shape.c()
-    return getattr(lib, fn)(ctypes.byref(cs), *[ctypes.c_void_p(p) if p else None for p in ptrs])
+    conv = [a if isinstance(a, int) and fn == "qsa_flash" and i == 9 else
+            (ctypes.c_void_p(a) if a else None) for i, a in enumerate(args)]
+    return getattr(lib, fn)(ctypes.byref(cs), *conv)
 
 
 @pytest.mark.parametrize("shape,expect", [
@@ -81,7 +102,8 @@ def test_bad_shapes_are_rejected(shape, expect):
     lib = qsa.load_library()
     s = qsa.QsaShape(**shape)
     fake = 0x10000  # never dereferenced: validation fails first
-    assert _raw(lib, "qsa_flash", s, fake, fake, fake, fake, fake, fake, fake, None, None) == expect
+    assert _raw(lib, "qsa_flash", s, fake, fake, fake, fake, fake, fake, fake, None, None, 0,
+                None) == expect
     assert _raw(lib, "qsa_topk", s, fake, fake, None) == expect
     assert _raw(lib, "qsa_merge", s, fake, fake, None) == expect
 
@@ -92,14 +114,14 @@ def test_null_and_misaligned_pointers_are_rejected():
     under = qsa.QsaShape(T=8, pos0=0)
     over = qsa.QsaShape(T=8, pos0=2050)
     E = qsa.QSA_ERR_ARG
-    # q, kq, ksc, vq, vsc, ids, out, part
-    assert _raw(lib, "qsa_flash", under, 0, A, A, A, A, 0, A, 0, None) == E
-    assert _raw(lib, "qsa_flash", under, A + 8, A, A, A, A, 0, A, 0, None) == E   # q 16 B
-    assert _raw(lib, "qsa_flash", under, A, A, A + 4, A, A, 0, A, 0, None) == E   # ksc 8 B
-    assert _raw(lib, "qsa_flash", under, A, A, A, A, A, 0, 0, 0, None) == E       # no out
-    assert _raw(lib, "qsa_flash", over, A, A, A, A, A, 0, A, 0, None) == E        # ids needed
-    assert _raw(lib, "qsa_flash", over, A, A, A, A, A, A + 2, A, 0, None) == E    # ids 4 B
-    assert _raw(lib, "qsa_flash", under, A, A, A, A, A, 0, 0, A + 8, None) == E   # part 16 B
+    # q, kq, ksc, vq, vsc, ids, out, part, workspace, workspace_bytes
+    assert _raw(lib, "qsa_flash", under, 0, A, A, A, A, 0, A, 0, None, 0, None) == E
+    assert _raw(lib, "qsa_flash", under, A + 8, A, A, A, A, 0, A, 0, None, 0, None) == E   # q 16 B
+    assert _raw(lib, "qsa_flash", under, A, A, A + 4, A, A, 0, A, 0, None, 0, None) == E   # ksc 8 B
+    assert _raw(lib, "qsa_flash", under, A, A, A, A, A, 0, 0, 0, None, 0, None) == E       # no out
+    assert _raw(lib, "qsa_flash", over, A, A, A, A, A, 0, A, 0, None, 0, None) == E        # ids needed
+    assert _raw(lib, "qsa_flash", over, A, A, A, A, A, A + 2, A, 0, None, 0, None) == E    # ids 4 B
+    assert _raw(lib, "qsa_flash", under, A, A, A, A, A, 0, 0, A + 8, None, 0, None) == E   # part 16 B
     assert _raw(lib, "qsa_topk", over, 0, A, None) == E                           # scores
     assert _raw(lib, "qsa_topk", under, 0, 0, None) == E                          # ids
     assert _raw(lib, "qsa_merge", under, A, A + 2, None) == E

@@ -95,6 +95,20 @@ def test_small_budgets_and_ragged_chunks(T, pos0, budget):
     _check(gpu_flash(inp, ids), ref)
 
 
+@pytest.mark.parametrize("T,pos0,spare", [(37, 0, 50), (25, 2040, 300)])
+def test_kv_history_with_spare_cells(T, pos0, spare):
+    # n_cells > pos0 + T: rows are n_cells apart and cells past n_kv are
+    # never read into the result (they hold large values here)
+    inp = qsa_synth.layer_inputs(T, pos0, seed=T, n_cells=pos0 + T + spare,
+                                 with_scores=pos0 + T > 2051)
+    inp.vq[:, pos0 + T:] = 127
+    inp.vsc[:, pos0 + T:] = np.float16(1000.0)
+    inp.ksc[:, pos0 + T:] = np.float16(1000.0)
+    ids = oracle.select(T, pos0, inp.budget, inp.scores, 2, inp.n_cells) \
+        if inp.scores is not None else None
+    _check(gpu_flash(inp, ids), oracle.attend(inp, ids))
+
+
 def test_single_cell_token_returns_its_value():
     inp = qsa_synth.layer_inputs(1, 0, seed=21)
     got = gpu_flash(inp)
