@@ -3,23 +3,33 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one prompt chunk pushed through the whole path for 12 layers:
-for the headline workload (T=1984 query tokens at pos0 0, 2 KV groups x 12
-heads, head dim 256, int8 K/V with fp16 per-64-dim scales) every token is
-under the 2051-cell budget, so its ids are the identity and are derived
-inside the attention kernel; a step is then 12 back-to-back qsa_flash
-dispatches, each over its own layer's seeded inputs (resident in HBM before
-the timed region).  The value is query tokens per second:
-T * steps / elapsed.
+Default workload (the headline): a prompt chunk of T=1984 query tokens at
+pos0 0 through 12 layers, 2 KV groups x 12 query heads, head dim 256, int8
+K/V codes with fp16 per-64-dim scales, budget 2051.  Every token sees at
+most 1984 cells, so its ids are the identity, derived on the device, and
+the host issues no selection call (the pages' host skips it for such
+prompts); a step is then 12 back-to-back qsa_flash calls, each on its own
+layer's seeded inputs, resident in HBM before the timed region.  The value
+is query tokens per second, T * steps / elapsed.
+
+Other workloads (--workload):
+  t512_pos0_x12, t1024_pos0_x12   the same at T = 512 / 1024;
+  t1984_pos30000                  long context: per step one layer of
+                                  qsa_topk (top 2051 of up to 31,984
+                                  cells) + qsa_flash with explicit ids;
+  decode4_pos8192                 4 tokens at position 8192: qsa_topk,
+                                  split qsa_flash, qsa_merge.
 
 One JSON line goes to stdout; progress goes to stderr.  The line carries
-`roofline` for the attention kernel (algorithmic gathered bytes per launch
-over its mean launch time, measured with HIP events on the launch stream)
-and `cpu_baseline` (the fp64 oracle on this host, a bounded sample).
+`roofline` for the attention call (algorithmic gathered bytes per launch
+over its mean duration, measured with HIP events on the launch stream),
+`mfma` (algorithmic flops over the same time) and `cpu_baseline` (the fp64
+oracle on this host, a bounded sample).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,13 +39,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
-LAYERS = 12
 BYTES_PER_VISIT = 2 * 256 + 2 * 4 * 2   # int8 K + V codes, 4 fp16 K + 4 fp16 V scales
 ID_BYTES_PER_VISIT = 4                  # int32 id read for rows above budget
 ROW_BYTES = 2 * (12 * 256 * 2)          # fp16 Q in + fp16 O out per (token, group)
 FLOPS_PER_VISIT = 12 * 256 * 2 * 2      # 12 heads x (QK^T + PV) x 2 flop per MAC
+# The pages' own figure for this metric: 12 qsa_flash layers at T=1984, pos0
+# 0 in 272.54 ms on an Apple M5 ("opus_r9_qsa", result table).  Context only.
+PAGES_M5_TOKS = {1984: 1984 / 0.27254, 1024: 1024 / 0.07533, 512: 512 / 0.02068}
+
+WORKLOADS = {
+    "t1984_pos0_x12": dict(T=1984, pos0=0, layers=12, kind="prompt"),
+    "t1024_pos0_x12": dict(T=1024, pos0=0, layers=12, kind="prompt"),
+    "t512_pos0_x12": dict(T=512, pos0=0, layers=12, kind="prompt"),
+    "t1984_pos30000": dict(T=1984, pos0=30000, layers=1, kind="prompt"),
+    "decode4_pos8192": dict(T=4, pos0=8192, layers=1, kind="decode"),
+}
+KERNEL_SOURCES = ("qsa_flash_tile.hip", "qsa_flash_rows.hip", "qsa_device.h")
 
 
 def log(*a):
@@ -56,41 +77,66 @@ def algorithmic(T: int, pos0: int, budget: int, G: int = 2):
     return visits, by, visits * FLOPS_PER_VISIT
 
 
-def cpu_baseline(T: int, pos0: int, target_s: float = 12.0, max_layers: int = 3):
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_sparse_flash_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{"):
+                rec = json.loads(line)
+    if not rec or rec.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(T: int, pos0: int, layers: int, target_s: float = 12.0, max_layers: int = 3):
     """The fp64 oracle on this host: whole layers of the same workload until
-    about target_s seconds have passed; scaled to query tokens/s for 12
-    layers."""
+    about target_s seconds have passed; scaled to query tokens/s for the
+    workload's layer count."""
     import oracle
     import qsa_synth
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     done, t_total = 0, 0.0
-    while done < max_layers and t_total < target_s:
+    while done < min(max_layers, layers) and t_total < target_s:
         inp = qsa_synth.layer_inputs(T, pos0, layer=done)
         ids = None
+        t0 = time.perf_counter()
         if inp.scores is not None:
             ids = oracle.select(T, pos0, inp.budget, inp.scores, 2, inp.n_cells)
-        t0 = time.perf_counter()
-        if ids is None:
-            oracle.attend(inp, None)
-        else:
-            oracle.attend(inp, ids)
+        oracle.attend(inp, ids)
         t_total += time.perf_counter() - t0
         done += 1
-    tok_s = T * done / t_total / LAYERS
-    return {"value": tok_s, "unit": "query-tokens/s (12 layers)", "cores": threads,
+    tok_s = T * done / t_total / layers
+    return {"value": tok_s, "unit": "query-tokens/s (%d layers)" % layers, "cores": threads,
             "kind": "oracle",
-            "sample": "%d of the 12 layers (all %d tokens each, T=%d pos0=%d), fp64 oracle "
-                      "attention, %.1f s wall; scaled by 1/12" % (done, T, T, pos0, t_total)}
+            "sample": "%d of the %d layers (all %d tokens each, T=%d pos0=%d), fp64 oracle "
+                      "selection + attention, %.1f s wall; scaled by 1/%d"
+                      % (done, layers, T, T, pos0, t_total, layers)}
 
 
 def main():
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--T", type=int, default=1984)
-    ap.add_argument("--pos0", type=int, default=0)
+    ap.add_argument("--workload", default="t1984_pos0_x12", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one device copy of this many MiB before timing (a known-size "
+                         "kernel for scaling FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path is built and timed on a single "
@@ -103,45 +149,70 @@ def main():
     import qsa_synth
     import quantized_sparse_flash_amd as qsa
 
-    T, pos0 = args.T, args.pos0
+    wl = WORKLOADS[args.workload]
+    T, pos0, L, kind = wl["T"], wl["pos0"], wl["layers"], wl["kind"]
     qsa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log("bench: generating %d layers of inputs (T=%d pos0=%d)" % (LAYERS, T, pos0))
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("bench: calibration copy of %d MiB done" % args.calib_copy_mb)
+
+    log("bench: generating %d layer(s) of inputs (%s)" % (L, args.workload))
     layers = []
-    for layer in range(LAYERS):
+    for layer in range(L):
         inp = qsa_synth.layer_inputs(T, pos0, layer=layer)
         d = {k: torch.from_numpy(np.ascontiguousarray(getattr(inp, k))).to(dev)
              for k in ("q", "kq", "ksc", "vq", "vsc")}
         s = qsa.QsaShape(T=T, pos0=pos0, n_groups=2, budget=inp.budget, n_cells=inp.n_cells)
+        d["scores"] = None if inp.scores is None else torch.from_numpy(inp.scores).to(dev)
         d["ids"] = None
         if inp.scores is not None:
-            sc = torch.from_numpy(inp.scores).to(dev)
             d["ids"] = torch.empty((T, 2, inp.budget), dtype=torch.int32, device=dev)
-            qsa.qsa_topk(s, sc, d["ids"])
-            del sc
         d["out"] = torch.empty((T, s.n_heads, 256), dtype=torch.float16, device=dev)
+        if kind == "decode":
+            d["part"] = torch.empty((T, s.n_part_chunks, s.n_heads, qsa.PART_STRIDE),
+                                    dtype=torch.float32, device=dev)
         d["shape"] = s
+        d["ws"] = qsa.flash_workspace(s, dev)
         layers.append(d)
+    # one workspace serves every layer: the calls run in order on one stream
+    ws = max((d["ws"] for d in layers if d["ws"] is not None), key=lambda t: t.numel(),
+             default=None)
     torch.cuda.synchronize()
     budget = layers[0]["shape"].budget
 
     def step(events=None):
         for i, d in enumerate(layers):
+            s = d["shape"]
+            if d["scores"] is not None:
+                qsa.qsa_topk(s, d["scores"], d["ids"])
             if events is not None:
                 events[i][0].record()
-            qsa.qsa_flash(d["shape"], d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"],
-                          d["out"])
+            if kind == "decode":
+                qsa.qsa_flash(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"], None,
+                              d["part"])
+            else:
+                qsa.qsa_flash(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"],
+                              d["out"], workspace=ws)
             if events is not None:
                 events[i][1].record()
+            if kind == "decode":
+                qsa.qsa_merge(s, d["part"], d["out"])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-launch events on the launch stream
+    # timed region: K steps; HIP events bracket each qsa_flash call on the
+    # stream it is launched on (torch's current stream)
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(LAYERS)] for _ in range(args.steps)]
+           for _ in range(L)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -156,11 +227,14 @@ def main():
     visits, by, flops = algorithmic(T, pos0, budget)
     gbs = by / mean_launch_s / 1e9
     tflops = flops / mean_launch_s / 1e12
-    log("bench: %.3f ms/step (12 layers), launch mean %.1f us, %.0f GB/s algorithmic, "
-        "%.1f TFLOP/s" % (ms_per_step, mean_launch_s * 1e6, gbs, tflops))
+    log("bench: %.3f ms/step, qsa_flash mean %.1f us, %.0f GB/s algorithmic, %.1f TFLOP/s"
+        % (ms_per_step, mean_launch_s * 1e6, gbs, tflops))
 
+    traffic = measured_traffic(args.workload)
+    m5 = PAGES_M5_TOKS.get(T) if (pos0 == 0 and L == 12) else None
+    steps_desc = {"prompt": "qsa_flash", "decode": "qsa_topk + split qsa_flash + qsa_merge"}
     line = {
-        "metric": "qsa_flash query-tokens/s at T=%d (12 layers)" % T,
+        "metric": "qsa_flash query-tokens/s at T=%d (%d layer%s)" % (T, L, "s" if L > 1 else ""),
         "value": value,
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -169,24 +243,33 @@ def main():
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": (value / m5) if m5 else None,
         "dtype": "int8 K/V codes, fp16 scales/Q/P/out, fp32 accumulate",
-        "data": "synthetic (seeded: q N(0,1) fp16, codes U[-127,127], scales U[0.002,0.02])",
-        "config": {"workload": "qsa_flash T=%d pos0=%d, 12 layers, 2 KV groups x 12 heads, "
-                               "head dim 256, budget %d" % (T, pos0, budget),
-                   "T": T, "pos0": pos0, "layers": LAYERS, "n_groups": 2,
-                   "heads_per_group": 12, "head_dim": 256, "budget": budget},
+        "data": "synthetic (seeded: q N(0,1) fp16, codes U[-127,127], scales U[0.002,0.02]"
+                "%s)" % (", scores N(0,1) fp32" if pos0 + T > budget else ""),
+        "config": {"workload": "%s: T=%d pos0=%d, %d layer(s) of %s%s, 2 KV groups x 12 "
+                               "heads, head dim 256, budget %d"
+                               % (args.workload, T, pos0, L,
+                                  "qsa_topk + " if (pos0 + T > budget and kind == "prompt")
+                                  else "", steps_desc[kind], budget),
+                   "T": T, "pos0": pos0, "layers": L, "n_groups": 2, "heads_per_group": 12,
+                   "head_dim": 256, "budget": budget},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "qsa flash attention",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "qsa_flash call (identity prefix: dequant prepass + tile "
+                               "kernel; rows above budget: row kernel)",
                      "algorithmic_bytes_per_launch": by, "cell_visits_per_launch": visits,
                      "mean_launch_us": mean_launch_s * 1e6},
-        "mfma": {"achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": tflops / MFMA_F16_PEAK_TFLOPS, "flops_per_launch": flops},
+        "mfma": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
+                 "flops_per_launch": flops},
     }
+    if m5:
+        line["vs_baseline_note"] = ("value / the pages' Apple M5 figure (%.0f query-tokens/s, "
+                                    "12 layers at T=%d); another machine, context only" % (m5, T))
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle (bounded sample)")
-        line["cpu_baseline"] = cpu_baseline(T, pos0)
+        line["cpu_baseline"] = cpu_baseline(T, pos0, L)
     print(json.dumps(line), flush=True)
 
 
