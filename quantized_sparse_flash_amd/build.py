@@ -38,6 +38,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
+           # no NaN inputs are supported (scores, codes and scales are finite),
+           # so max/min need no NaN canonicalisation; infinities are still used
+           "-fno-honor-nans",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", INCLUDE, "-o", tmp] + sources()
     if verbose:

@@ -29,11 +29,11 @@
 //     (global_load_lds_dwordx4, one chunk ahead, no registers held); each
 //     wave computes S^T[64 cells][32 queries] on v_mfma_f32_16x16x32_f16
 //     (A = K from LDS, B = Q^T held in registers), runs the online softmax on
-//     the accumulator registers (each lane owns one query: two cross-lane
-//     steps per max), moves its reference max only when a chunk exceeds it
-//     by more than 2^8 (so O is rarely rescaled; exact after the final
-//     division by l), and accumulates O^T[256 dims][32 queries] += V^T P^T
-//     with P taken straight from the S^T registers.
+//     the accumulator registers (each lane owns one query), takes the first
+//     chunk's max as its reference (later chunks never rescale O; a rare
+//     workgroup-wide fallback pass handles scores that outgrow it by 2^15),
+//     and accumulates O^T[256 dims][32 queries] += V^T P^T with P taken
+//     straight from the S^T registers.
 //
 // Workgroup i takes KV group i % G; with G = 2 and workgroups dealt to the
 // 8 XCDs round robin, each XCD's L2 holds one group's images only.
@@ -49,7 +49,7 @@ namespace {
 constexpr int kNT = 2;                      // 16-query N-tiles per wave
 constexpr int kSlots = 4 * 16 * kNT;        // query slots per workgroup
 constexpr int kTileTokens = kSlots / kHpg;  // whole tokens per workgroup (10)
-constexpr float kLazyRescale = 8.0f;        // log2 headroom of the running max
+constexpr float kMaxGrowth = 15.0f;         // log2 headroom above the reference max
 constexpr int kImgK = kChunk * kHeadDim * 2;  // bytes of the K image (32 KB)
 constexpr int kImgV = kHeadDim * kChunk * 2;  // bytes of the V^T image (32 KB)
 constexpr int kImg = kImgK + kImgV;           // bytes per (group, chunk) image
@@ -92,6 +92,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_copies_but(int n) {
   if (n == 0) wait_vmcnt<0>(); else wait_vmcnt<kCopyOps>();
+}
+
+// Max over the four 16-lane groups of a wave (lanes n, n+16, n+32, n+48),
+// on the VALU: v_permlane16_swap pairs rows {0,1} and {2,3}, then
+// v_permlane32_swap pairs the two halves.
+__device__ __forceinline__ float lane_group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Workgroup barrier without the memory wait __syncthreads() adds; the
@@ -203,8 +215,8 @@ __global__ __launch_bounds__(256) void dequant_chunks_kernel(RowArgs a, int n_ne
 // ---------------------------------------------------------------- attention
 __global__ __launch_bounds__(256, 1) void flash_tile_kernel(RowArgs a, int t_count, int nchunks,
                                                             const uint8_t* ws) {
-  __shared__ __attribute__((aligned(16))) uint8_t buf0[kImg];
-  __shared__ __attribute__((aligned(16))) uint8_t buf1[kImg];
+  __shared__ __attribute__((aligned(16))) uint8_t bufs[2 * kImg];  // chunk k in half k & 1
+  __shared__ int s_redo;  // set when the fast pass must be redone exactly
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.G, H = G * kHpg;
   const int n_blocks = (t_count + kTileTokens - 1) / kTileTokens;
@@ -249,148 +261,188 @@ __global__ __launch_bounds__(256, 1) void flash_tile_kernel(RowArgs a, int t_cou
     for (int i = 0; i < kCopyOps; ++i) copy16_to_lds(src + 1024 * i, dst + 1024 * i);
   };
 
-  f32x4 oacc[kNT][16];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < 16; ++mt) oacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[kNT], l_run[kNT];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-  }
-
-  // Barriers here are bare s_barrier: __syncthreads() would also wait for
-  // every outstanding global access, i.e. for the copy just issued.  Each
-  // wave consumes its LDS reads before a barrier, and waits for its own
-  // copies (vmcnt) before the barrier that publishes them.
-  // One step per chunk: chunk k is read from `kb` while chunk k+1 lands in
-  // `nb`.  Barriers here are bare s_barrier: __syncthreads() would also wait
-  // for every outstanding global access, i.e. for the copy just issued.
-  // Each wave consumes its LDS reads before a barrier, and waits for its own
-  // copies (vmcnt) before the barrier that publishes them.
-  auto step = [&](int k, const uint8_t* kb, uint8_t* nb) {
-    wg_barrier();  // every wave is done with chunk k-1, which lived in nb
-    if (k + 1 < nch) {
-      issue_copy(k + 1, nb);
-      wait_copies_but(kCopyOps);  // chunk k landed; chunk k+1 may be in flight
-    } else {
-      wait_copies_but(0);
-    }
-    wg_barrier();  // chunk k landed for every wave
-    const int cbase = k * kChunk;
-
-    // ---- S^T = K Q^T: k-step outer, 4 cell m-tiles x 2 query N-tiles inner
-    f32x4 sacc[kNT][4];
+  // One pass over the block's chunks.  Chunk k is read from its half of
+  // `bufs` while chunk k+1 lands in the other.  Barriers are bare s_barrier:
+  // __syncthreads() would also wait for every outstanding global access, i.e.
+  // for the copy just issued.  Each wave consumes its LDS reads before a
+  // barrier, and waits for its own copies (vmcnt) before the barrier that
+  // publishes them.
+  //
+  // Softmax reference.  Fast pass (SAFE = false): chunk 0 sets each query's
+  // reference max exactly (O is still zero); later chunks keep it, so O is
+  // never rescaled.  P = 2^(x - m) then stays below 2^kMaxGrowth unless a
+  // later score exceeds the reference by more than that; each lane records
+  // whether one did, and the workgroup votes at the end.  Safe pass (SAFE =
+  // true, only after such a vote): the exact online softmax, the running
+  // max updated every chunk and O rescaled when it moves.  Either way the
+  // result after the final division by l is the same softmax.
+  auto run = [&](auto SAFE_T) -> bool {
+    constexpr bool SAFE = decltype(SAFE_T)::value;
+    f32x4 oacc[kNT][16];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) sacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8_t af[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        af[mt] = *reinterpret_cast<const half8_t*>(
-            kb + kimg_off(16 * mt + n, 8 * (s >> 1) + 2 * j + (s & 1)));
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) sacc[nt][mt] = mfma16(af[mt], qf[nt][s], sacc[nt][mt]);
-    }
-
-    // ---- online softmax (base 2); masking only where the chunk reaches
-    // past the block's first token
-    const bool masked = cbase + kChunk > nkv_min;
-    half8_t pb[kNT][2];
-    bool grew = false;
-    float mnew[kNT];
+      for (int mt = 0; mt < 16; ++mt) oacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[kNT], l_run[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-      if (masked) {
+      m_run[nt] = -INFINITY;
+      l_run[nt] = 0.f;
+    }
+    bool over = false;
+
+    issue_copy(0, bufs);
+    for (int k = 0; k < nch; ++k) {
+      wg_barrier();  // every wave is done with chunk k-1, whose half gets chunk k+1
+      if (k + 1 < nch) {
+        issue_copy(k + 1, bufs + ((k + 1) & 1) * kImg);
+        wait_copies_but(kCopyOps);  // chunk k landed; chunk k+1 may be in flight
+      } else {
+        wait_copies_but(0);
+      }
+      wg_barrier();  // chunk k landed for every wave
+      const uint8_t* kb = bufs + (k & 1) * kImg;
+      const int cbase = k * kChunk;
+
+      // ---- S^T = K Q^T: k-step outer, 4 cell m-tiles x 2 query N-tiles inner
+      f32x4 sacc[kNT][4];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        half8_t af[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          af[mt] = *reinterpret_cast<const half8_t*>(
+              kb + kimg_off(16 * mt + n, 8 * (s >> 1) + 2 * j + (s & 1)));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (cbase + 16 * mt + 4 * j + r >= nkv_q[nt]) sacc[nt][mt][r] = -INFINITY;
+          for (int nt = 0; nt < kNT; ++nt) sacc[nt][mt] = mfma16(af[mt], qf[nt][s], sacc[nt][mt]);
       }
-      float cmax = -INFINITY;
+
+      // ---- scores to plain registers; masking (cells past a token's n_kv)
+      // only where the chunk reaches past the block's first token, against a
+      // per-lane limit so that the cell offsets are immediates
+      float sv[kNT][16];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        cmax = fmaxf(fmaxf(cmax, fmaxf(sacc[nt][mt][0], sacc[nt][mt][1])),
-                     fmaxf(sacc[nt][mt][2], sacc[nt][mt][3]));
-      cmax = wave_max_xor16_32(cmax) * kScoreScaleLog2;
-      // the reference max only moves when the chunk max exceeds it by more
-      // than kLazyRescale (log2 units): P then stays below 2^kLazyRescale
-      const bool up = cmax > m_run[nt] + kLazyRescale;
-      mnew[nt] = up ? cmax : m_run[nt];
-      grew |= up;
-    }
-    if (__builtin_amdgcn_ballot_w64(grew) != 0ull) {
-      // some reference max moved: rescale O and l (factor 1 for the others)
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sv[nt][4 * mt + r] = sacc[nt][mt][r];
+      if (cbase + kChunk > nkv_min) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const int lim = nkv_q[nt] - cbase - 4 * j;  // cell 16mt+4j+r valid iff 16mt+r < lim
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * mt + r >= lim) sv[nt][4 * mt + r] = -INFINITY;
+        }
+      }
+      float lmax[kNT];  // this lane's max over its 16 cells, raw score units
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
-        const float alpha = fast_exp2(m_run[nt] - mnew[nt]);
-        l_run[nt] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < 16; ++mt) oacc[nt][mt] *= alpha;
-        m_run[nt] = mnew[nt];
+        const float c0 = fmaxf(fmaxf(sv[nt][0], sv[nt][1]), fmaxf(sv[nt][2], sv[nt][3]));
+        const float c1 = fmaxf(fmaxf(sv[nt][4], sv[nt][5]), fmaxf(sv[nt][6], sv[nt][7]));
+        const float c2 = fmaxf(fmaxf(sv[nt][8], sv[nt][9]), fmaxf(sv[nt][10], sv[nt][11]));
+        const float c3 = fmaxf(fmaxf(sv[nt][12], sv[nt][13]), fmaxf(sv[nt][14], sv[nt][15]));
+        lmax[nt] = fmaxf(fmaxf(c0, c1), fmaxf(c2, c3));
       }
-    }
+      if constexpr (SAFE) {
+        bool grew = false;
+        float mnew[kNT];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      float lsum = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p = fast_exp2(
-              __builtin_fmaf(sacc[nt][2 * kk + (i >> 2)][i & 3], kScoreScaleLog2, -m_run[nt]));
-          lsum += p;
-          pb[nt][kk][i] = (_Float16)p;
+        for (int nt = 0; nt < kNT; ++nt) {
+          mnew[nt] = fmaxf(m_run[nt], lane_group_max(lmax[nt]) * kScoreScaleLog2);
+          grew |= mnew[nt] > m_run[nt];
         }
-      l_run[nt] += lsum;
-    }
-
-    // ---- O^T += V^T P^T: 16 dim m-tiles x 2 cell k-steps x 2 query N-tiles
+        if (__builtin_amdgcn_ballot_w64(grew) != 0ull) {
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) {
-      const int d = 16 * mt + n;
+          for (int nt = 0; nt < kNT; ++nt) {
+            const float alpha = fast_exp2(m_run[nt] - mnew[nt]);
+            l_run[nt] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 16; ++mt) oacc[nt][mt] *= alpha;
+            m_run[nt] = mnew[nt];
+          }
+        }
+      } else {
+        if (k == 0) {
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt)
+            m_run[nt] = lane_group_max(lmax[nt]) * kScoreScaleLog2;  // finite: cell 0 is valid
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt)
+            over |= lmax[nt] * kScoreScaleLog2 > m_run[nt] + kMaxGrowth;
+        }
+      }
+
+      // ---- P and O^T += V^T P^T, one 32-cell half (k-step kk) at a time, so
+      // the exponentials of the second half can overlap the first half's MFMAs
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const half8_t av = *reinterpret_cast<const half8_t*>(kb + vimg_off(d, 8 * kk + 2 * j));
+        half8_t pb[kNT];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) oacc[nt][mt] = mfma16(av, pb[nt][kk], oacc[nt][mt]);
+        for (int nt = 0; nt < kNT; ++nt) {
+          const float nm = -m_run[nt];
+          float lsum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float p = fast_exp2(__builtin_fmaf(sv[nt][8 * kk + i], kScoreScaleLog2, nm));
+            lsum += p;
+            pb[nt][i] = (_Float16)p;
+          }
+          l_run[nt] += lsum;
+        }
+#pragma unroll
+        for (int mt = 0; mt < 16; ++mt) {
+          const half8_t av =
+              *reinterpret_cast<const half8_t*>(kb + vimg_off(16 * mt + n, 8 * kk + 2 * j));
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) oacc[nt][mt] = mfma16(av, pb[nt], oacc[nt][mt]);
+        }
       }
     }
-    };
+
+    if constexpr (!SAFE) {
+      // workgroup vote: any score beyond the reference by more than
+      // 2^kMaxGrowth anywhere in the block sends the whole block to the safe
+      // pass (its result would still be finite, but P could have overflowed)
+      if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) s_redo = 1;
+      __syncthreads();
+      if (s_redo) return true;
+    }
+
+    // ---- finalise: O / l -> fp16; lane (n, j) holds dims 16*mt + 4*j + r
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const float l_tot = wave_sum_xor16_32(l_run[nt]);
+      if (!qvalid[nt]) continue;
+      const float inv = 1.f / l_tot;
+      _Float16* orow = a.out + ((int64_t)qt[nt] * H + qh[nt]) * kHeadDim + 4 * j;
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) {
+        half4_t h;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = (_Float16)(oacc[nt][mt][r] * inv);
+        *reinterpret_cast<half4_t*>(orow + 16 * mt) = h;
+      }
+    }
+    return false;
+  };
 
   // Q is in registers before any copy is issued: a compiler-visible wait, so
   // that no count-based wait for the Q loads is left inside the loop (it
   // would also wait for the copies, which the compiler does not count)
+  if (tid == 0) s_redo = 0;
   __builtin_amdgcn_s_waitcnt(0);
-  issue_copy(0, buf0);
-  for (int k = 0; k < nch; k += 2) {
-    step(k, buf0, buf1);
-    if (k + 1 < nch) step(k + 1, buf1, buf0);
-  }
-
-  // ---- finalise: O / l -> fp16; lane (n, j) holds dims 16*mt + 4*j + r
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const float l_tot = wave_sum_xor16_32(l_run[nt]);
-    if (!qvalid[nt]) continue;
-    const float inv = 1.f / l_tot;
-    _Float16* orow = a.out + ((int64_t)qt[nt] * H + qh[nt]) * kHeadDim + 4 * j;
-#pragma unroll
-    for (int mt = 0; mt < 16; ++mt) {
-      half4_t h;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = (_Float16)(oacc[nt][mt][r] * inv);
-      *reinterpret_cast<half4_t*>(orow + 16 * mt) = h;
-    }
-  }
+  if (run(std::false_type{})) run(std::true_type{});
 }
 
 int64_t tile_workspace_bytes(int G, int t_count, int pos0) {

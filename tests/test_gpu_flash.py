@@ -109,6 +109,18 @@ def test_kv_history_with_spare_cells(T, pos0, spare):
     _check(gpu_flash(inp, ids), oracle.attend(inp, ids))
 
 
+@pytest.mark.parametrize("late_scale", [0.03, 0.5])
+def test_scores_growing_after_the_first_chunk(late_scale):
+    # cells past the first 64 get larger K scales, so later chunks hold far
+    # larger scores than chunk 0: with 0.03 they stay within the kernels'
+    # fixed-reference headroom (P > 1), with 0.5 they exceed it and the
+    # exact rescaling pass must take over; both must match the oracle
+    inp = qsa_synth.layer_inputs(150, 0, seed=31)
+    inp.ksc[:, 64:] = np.float16(late_scale)
+    ref = oracle.attend(inp, None)
+    _check(gpu_flash(inp), ref)
+
+
 def test_single_cell_token_returns_its_value():
     inp = qsa_synth.layer_inputs(1, 0, seed=21)
     got = gpu_flash(inp)
