@@ -6,7 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/qsa.h"
+#include "qsa.h"
 #include "qsa_launch.h"
 
 

@@ -32,12 +32,6 @@
 
 namespace qsa {
 
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-  }(std::make_integer_sequence<int, N>{});
-}
 
 __device__ __forceinline__ half2_t splat_lo(uint32_t u) {
   const half2_t h = as_h2(u);

@@ -12,32 +12,53 @@
 // cells.  The path therefore dequantises each visible cell once per layer
 // and then runs a plain fp16 flash kernel over the result:
 //
-//   dequant_chunks_kernel  one workgroup per (group, 64-cell chunk): int8
-//     codes x fp16 scale -> fp16 (one SDWA convert + half a packed multiply
-//     per element: the value is rounded to fp16 once, as when the pages'
-//     kernel fills its K/V tiles), laid out in LDS as the 64 KB image the
-//     attention kernel consumes, then streamed to the workspace with
-//     coalesced 16-byte stores:  K [cell][dim] with 16-byte groups
-//     XOR-swizzled by cell, and V^T [dim][slot] with cells permuted inside
-//     each 32-cell half (so that one 16-byte read yields the eight cells an
-//     MFMA k-slot group needs) and 8-byte groups XOR-swizzled by dim.  Cells
-//     past the last visible one are zero.
+//   dequant_chunks_kernel  one workgroup per (group, 64-cell chunk, 32-cell
+//     half): int8 code x fp16 scale -> fp16 (the value is rounded to fp16
+//     once, as when the pages' kernel fills its K/V tiles), written to the
+//     workspace as the two 32 KB images the attention kernel copies verbatim
+//     into LDS:
+//       K    [64 cells][256 dims], the 16-byte group g of cell c's row at
+//            position g ^ (c & 15);
+//       V^T  [256 dims][64 slots]: 16-byte group 4 kk + j (kk = 32-cell half,
+//            j < 4) holds the cells 32 kk + 16 (e / 4) + 4 j + e % 4 for
+//            e = 0..7 (the eight cells an MFMA k-slot group needs, see
+//            below), and group g of dim d's row sits at position
+//            g ^ ((d >> 1) & 7).
+//     Both swizzles make the 16-byte MFMA operand reads conflict-free for
+//     any 16 consecutive rows.  Cells past the last visible one are zero.
 //
 //   flash_tile_kernel  one workgroup per (group, 10 tokens): 120 queries
-//     (10 tokens x 12 heads) on 4 waves x 32 query slots.  Chunk images
-//     stream from L2 straight into one of two LDS buffers
-//     (global_load_lds_dwordx4, one chunk ahead, no registers held); each
-//     wave computes S^T[64 cells][32 queries] on v_mfma_f32_16x16x32_f16
-//     (A = K from LDS, B = Q^T held in registers), runs the online softmax on
-//     the accumulator registers (each lane owns one query), takes the first
-//     chunk's max as its reference (later chunks never rescale O; a rare
-//     workgroup-wide fallback pass handles scores that outgrow it by 2^15),
-//     and accumulates O^T[256 dims][32 queries] += V^T P^T with P taken
-//     straight from the S^T registers.
+//     (10 tokens x 12 heads) on 8 waves x 16 query slots, two waves per
+//     SIMD, so that one wave's softmax runs on the VALU while the other's
+//     products occupy the matrix core.  Products on v_mfma_f32_16x16x32_f16
+//     with queries in the N dimension:
+//       S^T[64 cells][16 queries] = K Q^T   (A = K from LDS, B = Q^T held in
+//                                            registers for the whole block)
+//       O^T[256 dims][16 queries] += V^T P^T (A = V^T from LDS, B = P^T taken
+//                                            straight from the S^T registers)
+//     Lane l owns query l % 16 and the cells 16 mt + 4 (l / 16) + i of the
+//     chunk (mt, i < 4): row max and sum take two cross-lane steps, and the
+//     S^T registers of two consecutive 16-cell tiles are exactly the B
+//     operand of one 32-cell PV k-step once V^T uses the slot order above.
+//
+//     Software pipeline, one barrier per chunk: each wave issues chunk k+1's
+//     score MFMAs before chunk k's softmax, then chunk k's PV.  K and V^T
+//     images have separate double buffers: at chunk k the kernel reads K(k+1)
+//     and V(k) while K(k+2) and V(k+1) stream from L2 into the free halves
+//     (global_load_lds_dwordx4, no registers held).
+//
+//     Softmax reference.  The first chunk sets each query's reference max
+//     exactly; later chunks keep it, so O is never rescaled.  P = 2^(x - m)
+//     then stays below 2^kMaxGrowth unless a later score exceeds the
+//     reference by more than that; lanes record whether one did, and the
+//     workgroup votes at the end.  After such a vote (rare) the block is
+//     recomputed by an exact online-softmax pass that moves the running max
+//     and rescales O.  Either way the result after the final division by l
+//     is the same softmax.
 //
 // Workgroup i takes KV group i % G; with G = 2 and workgroups dealt to the
 // 8 XCDs round robin, each XCD's L2 holds one group's images only.
-#include <utility>
+#include <type_traits>
 
 #include "qsa_device.h"
 #include "qsa_launch.h"
@@ -46,17 +67,20 @@ namespace qsa {
 
 namespace {
 
-constexpr int kNT = 2;                      // 16-query N-tiles per wave
-constexpr int kSlots = 4 * 16 * kNT;        // query slots per workgroup
+constexpr int kWaves = 8;
+constexpr int kQpw = 16;                    // query slots per wave
+constexpr int kSlots = kQpw * kWaves;       // query slots per workgroup
 constexpr int kTileTokens = kSlots / kHpg;  // whole tokens per workgroup (10)
 constexpr float kMaxGrowth = 15.0f;         // log2 headroom above the reference max
-constexpr int kImgK = kChunk * kHeadDim * 2;  // bytes of the K image (32 KB)
-constexpr int kImgV = kHeadDim * kChunk * 2;  // bytes of the V^T image (32 KB)
-constexpr int kImg = kImgK + kImgV;           // bytes per (group, chunk) image
-constexpr int kCopyOps = kImg / 4 / 1024;     // 1 KB copies per wave per chunk (16)
+constexpr int kHalf = kChunk * kHeadDim * 2;  // bytes of one K or V^T image (32 KB)
+constexpr int kImg = 2 * kHalf;               // bytes per (group, chunk) in the workspace
+constexpr int kCopyOps = kHalf / 1024 / kWaves;  // 1 KB copies per wave per image (4)
+constexpr int kHalfCells = kChunk / 2;           // cells per dequant workgroup
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+typedef __attribute__((address_space(3))) const half8_t lds_half8_t;
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -68,8 +92,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Written as inline asm so that the compiler does not track the LDS write:
 // it would otherwise make every later LDS read wait for the copy to
 // complete, which serialises the prefetch with the math.  Completion is
-// awaited explicitly with wait_copies_but(), before a barrier publishes the
-// data.  The asm loads M0 itself; nothing else in this kernel uses M0 (DS
+// awaited explicitly (s_waitcnt vmcnt) before a barrier publishes the data.
+// The asm loads M0 itself; nothing else in this kernel uses M0 (DS
 // instructions on gfx9+ do not read it), so the clobber is harmless here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -83,28 +107,8 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds) {
       : "memory", "m0");
 }
 #pragma clang diagnostic pop
-// Wait until at most n of this wave's vector-memory operations (the copies
-// above, issued in order) are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory");
-}
-__device__ __forceinline__ void wait_copies_but(int n) {
-  if (n == 0) wait_vmcnt<0>(); else wait_vmcnt<kCopyOps>();
-}
-
-// Max over the four 16-lane groups of a wave (lanes n, n+16, n+32, n+48),
-// on the VALU: v_permlane16_swap pairs rows {0,1} and {2,3}, then
-// v_permlane32_swap pairs the two halves.
-__device__ __forceinline__ float lane_group_max(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
+// Wait until none of this wave's vector-memory operations is outstanding.
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
 // Workgroup barrier without the memory wait __syncthreads() adds; the
 // signal fences keep the compiler from moving memory accesses across it.
@@ -114,108 +118,100 @@ __device__ __forceinline__ void wg_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Max / sum over the four 16-lane groups of a wave (lanes n, n+16, n+32,
+// n+48), on the VALU: v_permlane16_swap pairs rows {0,1} and {2,3}, then
+// v_permlane32_swap pairs the two halves.
+__device__ __forceinline__ float lane_group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lane_group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Byte offset of the 16-byte group `grp` (8 dims) of K row `cell`.
 __device__ __forceinline__ int kimg_off(int cell, int grp) {
-  return cell * (kHeadDim * 2) + 16 * (grp ^ (cell & 7));
+  return cell * (kHeadDim * 2) + 16 * (grp ^ (cell & 15));
 }
-// Slot of chunk cell c in a V^T row: inside each 32-cell half, cells
-// {4j..4j+3, 16+4j..16+4j+3} become the consecutive slots 8j..8j+7 (the k
-// slots of lane group j in one 32-cell MFMA k-step).
-__device__ __forceinline__ int vperm(int c) {
-  const int kk = c >> 5, cc = c & 31;
-  return 32 * kk + 8 * ((cc & 15) >> 2) + 4 * (cc >> 4) + (cc & 3);
-}
-// Byte offset (inside the chunk image) of the 8-byte group `grp` (4 slots)
-// of V^T row d; the XOR is even, so 16-byte pairs of groups stay adjacent.
+// Byte offset of the 16-byte group `grp` (8 slots) of V^T row `d`.
 __device__ __forceinline__ int vimg_off(int d, int grp) {
-  return kImgK + d * (kChunk * 2) + 8 * (grp ^ (2 * ((d & 7) ^ ((d >> 4) & 7))));
+  return d * (kChunk * 2) + 16 * (grp ^ ((d >> 1) & 7));
+}
+// Cell (inside its 32-cell half) of V^T slot e of k-slot group j.
+__host__ __device__ constexpr int vslot_cell(int j, int e) {
+  return 16 * (e >> 2) + 4 * j + (e & 3);
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------- dequant
+// One workgroup per (group, chunk, 32-cell half).  Every thread loads 16
+// consecutive codes (a cell row is 16 lanes x 16 bytes) and the scale of two
+// cells, for K and for V; K goes straight to its image, V is transposed
+// through LDS so that each thread then writes one dim's four slot groups.
 __global__ __launch_bounds__(256) void dequant_chunks_kernel(RowArgs a, int n_needed,
                                                              int nchunks, uint8_t* ws) {
-  __shared__ __attribute__((aligned(16))) uint8_t img[kImg];
+  __shared__ _Float16 vt[kHeadDim][kHalfCells + 2];  // [dim][cell], padded rows
   const int tid = threadIdx.x;
-  const int g = blockIdx.x / nchunks, k = blockIdx.x % nchunks;
-  const int cbase = k * kChunk;
-  const int8_t* kq_g = a.kq + (int64_t)g * a.n_cells * kHeadDim;
-  const int8_t* vq_g = a.vq + (int64_t)g * a.n_cells * kHeadDim;
-  const _Float16* ksc_g = a.ksc + (int64_t)g * a.n_cells * kNBlk;
-  const _Float16* vsc_g = a.vsc + (int64_t)g * a.n_cells * kNBlk;
-
-  // K: units (cell, 16 dims): cell tid/16 + 16i, segment tid%16
-  {
-    const int seg = tid & 15;
-    u32x4 raw[4];
-    uint32_t sr[4];
+  const int kk = blockIdx.x & 1;  // 32-cell half of the chunk
+  const int gk = blockIdx.x >> 1;  // (group, chunk)
+  const int g = gk / nchunks, k = gk % nchunks;
+  const int cb = k * kChunk + kHalfCells * kk;
+  uint8_t* img = ws + (int64_t)gk * kImg;
+  const int seg = tid & 15;  // dims 16 seg .. +15
+  auto code = [](const u32x4& raw, int byte) -> _Float16 {
+    return (_Float16)(int8_t)(raw[byte >> 2] >> (8 * (byte & 3)));
+  };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = (tid >> 4) + 16 * i;
-      const int cell = min(cbase + c, n_needed - 1);
-      raw[i] = *reinterpret_cast<const u32x4*>(kq_g + (int64_t)cell * kHeadDim + 16 * seg);
-      sr[i] = *reinterpret_cast<const uint16_t*>(ksc_g + (int64_t)cell * kNBlk + (seg >> 2));
+  for (int r = 0; r < 2; ++r) {
+    const int c = (tid >> 4) + 16 * r;  // cell cb + c
+    const int cell = cb + c;
+    const bool live = cell < n_needed;
+    const int64_t row = ((int64_t)g * a.n_cells + (live ? cell : 0)) * kHeadDim + 16 * seg;
+    const int64_t srow = ((int64_t)g * a.n_cells + (live ? cell : 0)) * kNBlk + (seg >> 2);
+    const u32x4 kraw = *reinterpret_cast<const u32x4*>(a.kq + row);
+    const u32x4 vraw = *reinterpret_cast<const u32x4*>(a.vq + row);
+    // cells past the last visible one are zero
+    const uint16_t kbits = live ? reinterpret_cast<const uint16_t*>(a.ksc)[srow] : (uint16_t)0;
+    const uint16_t vbits = live ? reinterpret_cast<const uint16_t*>(a.vsc)[srow] : (uint16_t)0;
+    const _Float16 ks = __builtin_bit_cast(_Float16, kbits);
+    const _Float16 vs = __builtin_bit_cast(_Float16, vbits);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      half8_t v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = code(kraw, 8 * half + e) * ks;
+      *reinterpret_cast<half8_t*>(img + kimg_off(kHalfCells * kk + c, 2 * seg + half)) = v;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = (tid >> 4) + 16 * i;
-      const bool live = cbase + c < n_needed;
-      const half2_t sc = as_h2(live ? (sr[i] | (sr[i] << 16)) : 0u);
-      uint32_t o[8];
-      dq4(raw[i].x, sc, o[0], o[1]);
-      dq4(raw[i].y, sc, o[2], o[3]);
-      dq4(raw[i].z, sc, o[4], o[5]);
-      dq4(raw[i].w, sc, o[6], o[7]);
-      *reinterpret_cast<u32x4*>(img + kimg_off(c, 2 * seg)) = u32x4{o[0], o[1], o[2], o[3]};
-      *reinterpret_cast<u32x4*>(img + kimg_off(c, 2 * seg + 1)) = u32x4{o[4], o[5], o[6], o[7]};
-    }
-  }
-  // V: units (4 cells 4*cg.., 16 dims 16*dg..), transposed into V^T rows
-  {
-    const int dg = tid & 15, cg = tid >> 4;
-    u32x4 raw[4];
-    uint32_t sr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cell = min(cbase + 4 * cg + i, n_needed - 1);
-      raw[i] = *reinterpret_cast<const u32x4*>(vq_g + (int64_t)cell * kHeadDim + 16 * dg);
-      const bool live = cbase + 4 * cg + i < n_needed;
-      sr[i] = live ? *reinterpret_cast<const uint16_t*>(vsc_g + (int64_t)cell * kNBlk + (dg >> 2))
-                   : 0u;
-    }
-    const half2_t s01 = as_h2(sr[0] | (sr[1] << 16));
-    const half2_t s23 = as_h2(sr[2] | (sr[3] << 16));
-    const int grp = vperm(4 * cg) >> 2;
-    auto put = [&](auto E, int d, uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
-      constexpr int e = decltype(E)::value;  // byte inside the dwords
-      const uint32_t lo = as_u32(col_pair<e>(w0, w1) * s01);
-      const uint32_t hi = as_u32(col_pair<e>(w2, w3) * s23);
-      *reinterpret_cast<u32x2*>(img + vimg_off(d, grp)) = u32x2{lo, hi};
-    };
-#pragma unroll
-    for (int dw = 0; dw < 4; ++dw) {
-      const uint32_t w0 = raw[0][dw], w1 = raw[1][dw], w2 = raw[2][dw], w3 = raw[3][dw];
-      const int d = 16 * dg + 4 * dw;
-      put(std::integral_constant<int, 0>{}, d + 0, w0, w1, w2, w3);
-      put(std::integral_constant<int, 1>{}, d + 1, w0, w1, w2, w3);
-      put(std::integral_constant<int, 2>{}, d + 2, w0, w1, w2, w3);
-      put(std::integral_constant<int, 3>{}, d + 3, w0, w1, w2, w3);
-    }
+    for (int e = 0; e < 16; ++e) vt[16 * seg + e][c] = code(vraw, e) * vs;
   }
   __syncthreads();
-  uint8_t* dst = ws + (int64_t)blockIdx.x * kImg;
+  const int d = tid;
 #pragma unroll
-  for (int i = 0; i < kImg / 16 / 256; ++i) {
-    const int off = 16 * (tid + 256 * i);
-    *reinterpret_cast<u32x4*>(dst + off) = *reinterpret_cast<const u32x4*>(img + off);
+  for (int j = 0; j < 4; ++j) {
+    half8_t v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = vt[d][vslot_cell(j, e)];
+    *reinterpret_cast<half8_t*>(img + kHalf + vimg_off(d, 4 * kk + j)) = v;
   }
 }
 
 // ---------------------------------------------------------------- attention
-__global__ __launch_bounds__(256, 1) void flash_tile_kernel(RowArgs a, int t_count, int nchunks,
-                                                            const uint8_t* ws) {
-  __shared__ __attribute__((aligned(16))) uint8_t bufs[2 * kImg];  // chunk k in half k & 1
+__global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, int t_count,
+                                                                    int nchunks,
+                                                                    const uint8_t* ws) {
+  // K(c) lives in kv[c & 1], V^T(c) in kv[2 + (c & 1)]
+  __shared__ __attribute__((aligned(16))) uint8_t kv[4 * kHalf];
   __shared__ int s_redo;  // set when the fast pass must be redone exactly
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.G, H = G * kHpg;
@@ -232,206 +228,287 @@ __global__ __launch_bounds__(256, 1) void flash_tile_kernel(RowArgs a, int t_cou
 
   const int n = lane & 15, j = lane >> 4;
 
-  // ---- per-lane queries: N-tile nt, column n -> query slot of the workgroup
-  int nkv_q[kNT];
-  bool qvalid[kNT];
-  int qt[kNT], qh[kNT];
-  half8_t qf[kNT][8];
+  // ---- this lane's query: slot kQpw w + n of the workgroup
+  const int qs = kQpw * w + n;
+  const int qt = t0 + qs / kHpg;
+  const int qh = g * kHpg + qs % kHpg;
+  const bool qvalid = qs < kTileTokens * kHpg && qt <= t_last;
+  const int nkv_q = qvalid ? a.pos0 + qt + 1 : 1;
+  half8_t qf[8];  // Q^T k-step s: dims 32 s + 8 j .. +7
+  {
+    const _Float16* qrow = a.q + ((int64_t)(qvalid ? qt : t0) * H + (qvalid ? qh : g * kHpg)) *
+                                     kHeadDim + 8 * j;
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const int q = 16 * kNT * w + 16 * nt + n;
-    const int t = t0 + q / kHpg;
-    qt[nt] = t;
-    qh[nt] = g * kHpg + q % kHpg;
-    qvalid[nt] = q < kTileTokens * kHpg && t <= t_last;
-    nkv_q[nt] = qvalid[nt] ? a.pos0 + t + 1 : 1;
-    const _Float16* qrow = a.q + ((int64_t)(qvalid[nt] ? t : t0) * H + qh[nt]) * kHeadDim;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int d0 = 64 * (s >> 1) + 16 * j + 8 * (s & 1);
-      qf[nt][s] = *reinterpret_cast<const half8_t*>(qrow + d0);
-    }
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const half8_t*>(qrow + 32 * s);
   }
 
-  // ---- chunk image k -> dbuf: wave w moves bytes [16 KB w, 16 KB (w+1))
-  auto issue_copy = [&](int k, uint8_t* dbuf) {
-    const uint8_t* src = img_g + (int64_t)k * kImg + w * (kImg / 4) + 16 * lane;
-    const uint32_t dst = lds_addr(dbuf) + w * (kImg / 4);
+  // ---- LDS read addresses of this lane's operand fragments
+  // K: row (cell) 16 mt + n, group 4 s + j; s = 4 v + u -> the XOR touches
+  // the low 4 bits only, so v and mt are immediates
+  uint32_t koff[4];
 #pragma unroll
-    for (int i = 0; i < kCopyOps; ++i) copy16_to_lds(src + 1024 * i, dst + 1024 * i);
+  for (int u = 0; u < 4; ++u) koff[u] = lds_addr(kv) + kimg_off(n, 4 * u + j);
+  // V^T: row (dim) 16 mt + n, group 4 kk + j
+  uint32_t voff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) voff[kk] = lds_addr(kv) + 2 * kHalf + vimg_off(n, 4 * kk + j);
+
+  auto issue_copy = [&](const uint8_t* src, uint32_t dst) {
+    const uint8_t* s = src + w * (kHalf / kWaves) + 16 * lane;
+    const uint32_t d = dst + w * (kHalf / kWaves);
+#pragma unroll
+    for (int i = 0; i < kCopyOps; ++i) copy16_to_lds(s + 1024 * i, d + 1024 * i);
+  };
+  auto copy_k = [&](int c) { issue_copy(img_g + (int64_t)c * kImg, lds_addr(kv) + (c & 1) * kHalf); };
+  auto copy_v = [&](int c) {
+    issue_copy(img_g + (int64_t)c * kImg + kHalf, lds_addr(kv) + (2 + (c & 1)) * kHalf);
   };
 
-  // One pass over the block's chunks.  Chunk k is read from its half of
-  // `bufs` while chunk k+1 lands in the other.  Barriers are bare s_barrier:
-  // __syncthreads() would also wait for every outstanding global access, i.e.
-  // for the copy just issued.  Each wave consumes its LDS reads before a
-  // barrier, and waits for its own copies (vmcnt) before the barrier that
-  // publishes them.
-  //
-  // Softmax reference.  Fast pass (SAFE = false): chunk 0 sets each query's
-  // reference max exactly (O is still zero); later chunks keep it, so O is
-  // never rescaled.  P = 2^(x - m) then stays below 2^kMaxGrowth unless a
-  // later score exceeds the reference by more than that; each lane records
-  // whether one did, and the workgroup votes at the end.  Safe pass (SAFE =
-  // true, only after such a vote): the exact online softmax, the running
-  // max updated every chunk and O rescaled when it moves.  Either way the
-  // result after the final division by l is the same softmax.
+  auto lds16 = [](uint32_t addr) -> half8_t { return *(const lds_half8_t*)(uintptr_t)addr; };
+
+  // S^T of the chunk whose K image sits in kv[KP] (KP = chunk parity)
+  auto scores = [&](auto KP_T, f32x4 (&sacc)[4]) {
+    constexpr int KP = decltype(KP_T)::value;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) sacc[mt] = zero4();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const half8_t af =
+            lds16(koff[s & 3] + (KP * kHalf + 256 * (s >> 2) + mt * 16 * (kHeadDim * 2)));
+        sacc[mt] = mfma16(af, qf[s], sacc[mt]);
+      }
+    }
+  };
+
+  // Mask cells past each query's n_kv (only chunks that reach past the
+  // block's first token need it).  Cell of (mt, i): 16 mt + 4 j + i.
+  auto mask = [&](int c, f32x4 (&sacc)[4]) {
+    const int cbase = c * kChunk;
+    if (cbase + kChunk > nkv_min) {
+      const int lim = nkv_q - cbase - 4 * j;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * mt + i >= lim) sacc[mt][i] = -INFINITY;
+    }
+  };
+
+  // max over this query's cells of the chunk, in scaled log2 units
+  auto chunk_max = [&](const f32x4 (&sacc)[4]) {
+    float m[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      m[mt] = fmaxf(fmaxf(sacc[mt][0], sacc[mt][1]), fmaxf(sacc[mt][2], sacc[mt][3]));
+    return lane_group_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]))) * kScoreScaleLog2;
+  };
+
+  // P = 2^(x - m) as fp16 B operands of the two 32-cell PV k-steps; adds
+  // the fp32 exponentials to l.  Slot e of k-step kk is S^T tile 2 kk + e/4,
+  // register e % 4.
+  auto probs = [&](const f32x4 (&sacc)[4], float m, float& l, half8_t (&pb)[2]) {
+    const float nm = -m;
+    float ls[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(__builtin_fmaf(sacc[2 * kk + (e >> 2)][e & 3], kScoreScaleLog2, nm));
+        pb[kk][e] = (_Float16)p[e];
+      }
+      ls[kk] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    l += ls[0] + ls[1];
+  };
+
+  // O^T += V^T P^T for the chunk whose V^T image sits in kv[2 + VP]
+  auto pv = [&](auto VP_T, const half8_t (&pb)[2], f32x4 (&oacc)[16]) {
+    constexpr int VP = decltype(VP_T)::value;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) {
+        const half8_t af = lds16(voff[kk] + (VP * kHalf + mt * 16 * (kChunk * 2)));
+        oacc[mt] = mfma16(af, pb[kk], oacc[mt]);
+      }
+  };
+
+  // One pass over the block's chunks; returns true when the fast pass must
+  // be redone exactly (SAFE = false only).
   auto run = [&](auto SAFE_T) -> bool {
     constexpr bool SAFE = decltype(SAFE_T)::value;
-    f32x4 oacc[kNT][16];
+    f32x4 oacc[16];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < 16; ++mt) oacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[kNT], l_run[kNT];
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      m_run[nt] = -INFINITY;
-      l_run[nt] = 0.f;
-    }
+    for (int mt = 0; mt < 16; ++mt) oacc[mt] = zero4();
+    float m_ref = -INFINITY, l_run = 0.f;
     bool over = false;
 
-    issue_copy(0, bufs);
-    for (int k = 0; k < nch; ++k) {
-      wg_barrier();  // every wave is done with chunk k-1, whose half gets chunk k+1
-      if (k + 1 < nch) {
-        issue_copy(k + 1, bufs + ((k + 1) & 1) * kImg);
-        wait_copies_but(kCopyOps);  // chunk k landed; chunk k+1 may be in flight
+    copy_k(0);
+    copy_v(0);
+    if (nch > 1) copy_k(1);
+    wait_vmcnt0();
+    wg_barrier();
+    f32x4 s_cur[4];
+    scores(std::integral_constant<int, 0>{}, s_cur);
+
+    // chunk c (parity P): (NEXT) the scores of c + 1, the softmax of c, PV of c
+    auto step = [&](int c, auto NEXT_T, auto P_T) {
+      constexpr bool NEXT = decltype(NEXT_T)::value;
+      constexpr int P = decltype(P_T)::value;
+      wait_vmcnt0();  // this wave's copies of K(c+1) and V(c) have landed
+      wg_barrier();   // ... every wave's; and nobody reads K(c) or V(c-1) any more
+      if (c + 2 < nch) copy_k(c + 2);
+      if (c + 1 < nch) copy_v(c + 1);
+      f32x4 s_nxt[4];
+      if constexpr (NEXT) scores(std::integral_constant<int, 1 - P>{}, s_nxt);
+      mask(c, s_cur);
+      const float cm = chunk_max(s_cur);
+      if constexpr (SAFE) {
+        const float m_new = fmaxf(m_ref, cm);
+        if (__builtin_amdgcn_ballot_w64(m_new > m_ref) != 0ull) {
+          const float alpha = fast_exp2(m_ref - m_new);  // 0 while m_ref = -inf
+          l_run *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < 16; ++mt) oacc[mt] *= alpha;
+          m_ref = m_new;
+        }
       } else {
-        wait_copies_but(0);
+        m_ref = c == 0 ? cm : m_ref;  // chunk 0 always holds cell 0: finite
+        over |= qvalid && cm > m_ref + kMaxGrowth;
       }
-      wg_barrier();  // chunk k landed for every wave
-      const uint8_t* kb = bufs + (k & 1) * kImg;
-      const int cbase = k * kChunk;
-
-      // ---- S^T = K Q^T: k-step outer, 4 cell m-tiles x 2 query N-tiles inner
-      f32x4 sacc[kNT][4];
+      half8_t pb[2];
+      probs(s_cur, m_ref, l_run, pb);
+      pv(std::integral_constant<int, P>{}, pb, oacc);
+      if constexpr (NEXT) {
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) sacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        half8_t af[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          af[mt] = *reinterpret_cast<const half8_t*>(
-              kb + kimg_off(16 * mt + n, 8 * (s >> 1) + 2 * j + (s & 1)));
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) sacc[nt][mt] = mfma16(af[mt], qf[nt][s], sacc[nt][mt]);
+        for (int mt = 0; mt < 4; ++mt) s_cur[mt] = s_nxt[mt];
       }
-
-      // ---- scores to plain registers; masking (cells past a token's n_kv)
-      // only where the chunk reaches past the block's first token, against a
-      // per-lane limit so that the cell offsets are immediates
-      float sv[kNT][16];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sv[nt][4 * mt + r] = sacc[nt][mt][r];
-      if (cbase + kChunk > nkv_min) {
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int lim = nkv_q[nt] - cbase - 4 * j;  // cell 16mt+4j+r valid iff 16mt+r < lim
+    };
+    // The same chunk for the fast pass, as an explicit schedule of stages
+    // of four MFMAs: the operand fragments of stage i + 2 are read while
+    // stage i multiplies, the softmax exponentials of chunk c are spread
+    // over the score stages, and scheduler fences keep that order.
+    auto step_fast = [&](int c, auto NEXT_T, auto P_T) {
+      constexpr bool NEXT = decltype(NEXT_T)::value;
+      constexpr int P = decltype(P_T)::value;
+      constexpr int kS = NEXT ? 8 : 0;  // score stages (k-steps of chunk c + 1)
+      constexpr int kStages = kS + 8;   // then PV stages: k-step t / 4, m-tiles 4 (t % 4) ..
+      wait_vmcnt0();  // this wave's copies of K(c+1) and V(c) have landed
+      wg_barrier();   // ... every wave's; and nobody reads K(c) or V(c-1) any more
+      if (c + 2 < nch) copy_k(c + 2);
+      if (c + 1 < nch) copy_v(c + 1);
+      mask(c, s_cur);
+      half8_t fr[3][4];
+      auto load = [&](auto I, half8_t (&dst)[4]) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < kS) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (16 * mt + r >= lim) sv[nt][4 * mt + r] = -INFINITY;
-        }
-      }
-      float lmax[kNT];  // this lane's max over its 16 cells, raw score units
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const float c0 = fmaxf(fmaxf(sv[nt][0], sv[nt][1]), fmaxf(sv[nt][2], sv[nt][3]));
-        const float c1 = fmaxf(fmaxf(sv[nt][4], sv[nt][5]), fmaxf(sv[nt][6], sv[nt][7]));
-        const float c2 = fmaxf(fmaxf(sv[nt][8], sv[nt][9]), fmaxf(sv[nt][10], sv[nt][11]));
-        const float c3 = fmaxf(fmaxf(sv[nt][12], sv[nt][13]), fmaxf(sv[nt][14], sv[nt][15]));
-        lmax[nt] = fmaxf(fmaxf(c0, c1), fmaxf(c2, c3));
-      }
-      if constexpr (SAFE) {
-        bool grew = false;
-        float mnew[kNT];
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          mnew[nt] = fmaxf(m_run[nt], lane_group_max(lmax[nt]) * kScoreScaleLog2);
-          grew |= mnew[nt] > m_run[nt];
-        }
-        if (__builtin_amdgcn_ballot_w64(grew) != 0ull) {
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) {
-            const float alpha = fast_exp2(m_run[nt] - mnew[nt]);
-            l_run[nt] *= alpha;
-#pragma unroll
-            for (int mt = 0; mt < 16; ++mt) oacc[nt][mt] *= alpha;
-            m_run[nt] = mnew[nt];
-          }
-        }
-      } else {
-        if (k == 0) {
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
-            m_run[nt] = lane_group_max(lmax[nt]) * kScoreScaleLog2;  // finite: cell 0 is valid
+            dst[mt] = lds16(koff[i & 3] +
+                            ((1 - P) * kHalf + 256 * (i >> 2) + mt * 16 * (kHeadDim * 2)));
         } else {
+          constexpr int t = i - kS;
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
-            over |= lmax[nt] * kScoreScaleLog2 > m_run[nt] + kMaxGrowth;
+          for (int m = 0; m < 4; ++m)
+            dst[m] = lds16(voff[t >> 2] + (P * kHalf + (4 * (t & 3) + m) * 16 * (kChunk * 2)));
         }
+      };
+      f32x4 s_nxt[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) s_nxt[mt] = zero4();
+      load(std::integral_constant<int, 0>{}, fr[0]);
+      load(std::integral_constant<int, 1>{}, fr[1]);
+      const float cm = chunk_max(s_cur);
+      m_ref = c == 0 ? cm : m_ref;  // chunk 0 always holds cell 0: finite
+      over |= qvalid && cm > m_ref + kMaxGrowth;
+      const float nm = -m_ref;
+      float p[16];  // exponentials in B-operand slot order: 8 kk + e
+      half8_t pb[2];
+      auto expo = [&](int q) {
+        const int kk = q >> 3, e = q & 7;
+        p[q] = fast_exp2(__builtin_fmaf(s_cur[2 * kk + (e >> 2)][e & 3], kScoreScaleLog2, nm));
+      };
+      auto pack = [&](int kk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[kk][e] = (_Float16)p[8 * kk + e];
+        l_run += ((p[8 * kk] + p[8 * kk + 1]) + (p[8 * kk + 2] + p[8 * kk + 3])) +
+                 ((p[8 * kk + 4] + p[8 * kk + 5]) + (p[8 * kk + 6] + p[8 * kk + 7]));
+      };
+      if constexpr (!NEXT) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) expo(q);
+        pack(0);
       }
-
-      // ---- P and O^T += V^T P^T, one 32-cell half (k-step kk) at a time, so
-      // the exponentials of the second half can overlap the first half's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<kStages>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i + 2 < kStages) load(std::integral_constant<int, i + 2>{}, fr[(i + 2) % 3]);
+        if constexpr (i < kS) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        half8_t pb[kNT];
+          for (int mt = 0; mt < 4; ++mt) s_nxt[mt] = mfma16(fr[i % 3][mt], qf[i], s_nxt[mt]);
+          expo(2 * i);
+          expo(2 * i + 1);
+          if constexpr (i == 3) pack(0);
+          if constexpr (i == 7) pack(1);
+        } else {
+          constexpr int t = i - kS;
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const float nm = -m_run[nt];
-          float lsum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float p = fast_exp2(__builtin_fmaf(sv[nt][8 * kk + i], kScoreScaleLog2, nm));
-            lsum += p;
-            pb[nt][i] = (_Float16)p;
+          for (int m = 0; m < 4; ++m)
+            oacc[4 * (t & 3) + m] = mfma16(fr[i % 3][m], pb[t >> 2], oacc[4 * (t & 3) + m]);
+          if constexpr (!NEXT && t < 4) {
+            expo(8 + 2 * t);
+            expo(9 + 2 * t);
+            if constexpr (t == 3) pack(1);
           }
-          l_run[nt] += lsum;
         }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr (NEXT) {
 #pragma unroll
-        for (int mt = 0; mt < 16; ++mt) {
-          const half8_t av =
-              *reinterpret_cast<const half8_t*>(kb + vimg_off(16 * mt + n, 8 * kk + 2 * j));
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) oacc[nt][mt] = mfma16(av, pb[nt], oacc[nt][mt]);
-        }
+        for (int mt = 0; mt < 4; ++mt) s_cur[mt] = s_nxt[mt];
       }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    auto any_step = [&](int c, auto NEXT_T, auto P_T) {
+      if constexpr (SAFE) step(c, NEXT_T, P_T); else step_fast(c, NEXT_T, P_T);
+    };
+    int c = 0;
+    for (; c + 2 < nch; c += 2) {
+      any_step(c, T_{}, P0{});
+      any_step(c + 1, T_{}, P1{});
+    }
+    if (c + 1 < nch) {
+      any_step(c, T_{}, P0{});
+      any_step(c + 1, F_{}, P1{});
+    } else {
+      any_step(c, F_{}, P0{});
     }
 
     if constexpr (!SAFE) {
-      // workgroup vote: any score beyond the reference by more than
-      // 2^kMaxGrowth anywhere in the block sends the whole block to the safe
-      // pass (its result would still be finite, but P could have overflowed)
-      if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) s_redo = 1;
+      // workgroup vote: a score beyond the reference by more than
+      // 2^kMaxGrowth anywhere in the block sends it to the exact pass
+      if (__builtin_amdgcn_ballot_w64(over) != 0ull) s_redo = 1;
       __syncthreads();
       if (s_redo) return true;
     }
 
-    // ---- finalise: O / l -> fp16; lane (n, j) holds dims 16*mt + 4*j + r
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      const float l_tot = wave_sum_xor16_32(l_run[nt]);
-      if (!qvalid[nt]) continue;
+    // ---- finalise: O / l -> fp16; lane (n, j) holds dims 16 mt + 4 j + i
+    const float l_tot = lane_group_sum(l_run);
+    if (qvalid) {
       const float inv = 1.f / l_tot;
-      _Float16* orow = a.out + ((int64_t)qt[nt] * H + qh[nt]) * kHeadDim + 4 * j;
+      _Float16* orow = a.out + ((int64_t)qt * H + qh) * kHeadDim + 4 * j;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
-        half4_t h;
+        half4_t o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = (_Float16)(oacc[nt][mt][r] * inv);
-        *reinterpret_cast<half4_t*>(orow + 16 * mt) = h;
+        for (int i = 0; i < 4; ++i) o[i] = (_Float16)(oacc[mt][i] * inv);
+        *reinterpret_cast<half4_t*>(orow + 16 * mt) = o;
       }
     }
     return false;
@@ -442,6 +519,7 @@ __global__ __launch_bounds__(256, 1) void flash_tile_kernel(RowArgs a, int t_cou
   // would also wait for the copies, which the compiler does not count)
   if (tid == 0) s_redo = 0;
   __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   if (run(std::false_type{})) run(std::true_type{});
 }
 
@@ -457,11 +535,13 @@ hipError_t launch_flash_tile(const RowArgs& a, int t_count, void* ws, hipStream_
   const int n_needed = a.pos0 + t_count;
   const int nchunks = (n_needed + kChunk - 1) / kChunk;
   uint8_t* img = static_cast<uint8_t*>(ws);
-  dequant_chunks_kernel<<<dim3(a.G * nchunks), dim3(256), 0, stream>>>(a, n_needed, nchunks, img);
+  dequant_chunks_kernel<<<dim3(a.G * nchunks * 2), dim3(256), 0, stream>>>(a, n_needed, nchunks,
+                                                                           img);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_blocks = (t_count + kTileTokens - 1) / kTileTokens;
-  flash_tile_kernel<<<dim3(n_blocks * a.G), dim3(256), 0, stream>>>(a, t_count, nchunks, img);
+  flash_tile_kernel<<<dim3(n_blocks * a.G), dim3(kWaves * 64), 0, stream>>>(a, t_count, nchunks,
+                                                                           img);
   return hipGetLastError();
 }
 
