@@ -124,6 +124,29 @@ int qsa_flash(const qsa_shape *shape, const _Float16 *q, const int8_t *kq, const
               float *part, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * qsa_flash_prepare, qsa_flash_attend -- the two halves of a fused-mode
+ * qsa_flash call, for callers that time or schedule them apart.  The fused
+ * path first dequantises the cells that every token under budget reads (the
+ * shared identity prefix, see qsa_flash_workspace_bytes) into `workspace`,
+ * then attends.  qsa_flash_prepare enqueues the first half only (nothing
+ * when no token is under budget); qsa_flash_attend enqueues the second
+ * half and reads the workspace that a qsa_flash_prepare call with the same
+ * shape and K/V arguments filled earlier on the same stream (or one ordered
+ * before it).  The pair computes exactly what one fused qsa_flash call
+ * computes, and qsa_flash (fused mode) is these two calls.  Arguments,
+ * alignment and error behaviour are those of qsa_flash; `out` is written by
+ * qsa_flash_attend.  Attending without a prepared workspace gives
+ * unspecified output values (never an out-of-bounds access).
+ */
+int qsa_flash_prepare(const qsa_shape *shape, const int8_t *kq, const _Float16 *ksc,
+                      const int8_t *vq, const _Float16 *vsc, void *workspace,
+                      int64_t workspace_bytes, void *stream);
+int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq,
+                     const _Float16 *ksc, const int8_t *vq, const _Float16 *vsc,
+                     const int32_t *ids, _Float16 *out, void *workspace,
+                     int64_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace qsa_flash needs for this shape in fused mode
  * (0 when no token is under budget, and split mode needs none); a host-only
  * helper.  The fused path dequantises the cells that tokens under budget

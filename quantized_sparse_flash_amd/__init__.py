@@ -10,6 +10,8 @@ the library is missing or cannot be loaded, calls raise.
 Entry points (all asynchronous on the current stream):
   qsa_topk(shape, scores, ids)                                 selection
   qsa_flash(shape, q, kq, ksc, vq, vsc, ids, out, part=None)   attention
+  qsa_flash_prepare(shape, kq, ksc, vq, vsc, workspace)         fused mode, first half
+  qsa_flash_attend(shape, q, kq, ksc, vq, vsc, ids, out, workspace)   ... second half
   qsa_merge(shape, part, out)                                  LSE merge
 """
 from __future__ import annotations
@@ -34,8 +36,8 @@ PART_STRIDE = 258
 DEFAULT_BUDGET = 2051
 MAX_BUDGET = 65536
 
-EXPORTED = ("qsa_topk", "qsa_flash", "qsa_merge", "qsa_status_string", "qsa_part_elems",
-            "qsa_flash_workspace_bytes")
+EXPORTED = ("qsa_topk", "qsa_flash", "qsa_flash_prepare", "qsa_flash_attend", "qsa_merge",
+            "qsa_status_string", "qsa_part_elems", "qsa_flash_workspace_bytes")
 
 
 class QsaError(RuntimeError):
@@ -96,6 +98,8 @@ def load_library(path: str = LIB_PATH):
     SP = ctypes.POINTER(_CShape)
     lib.qsa_topk.argtypes = [SP, P, P, P]
     lib.qsa_flash.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]
+    lib.qsa_flash_prepare.argtypes = [SP, P, P, P, P, P, ctypes.c_int64, P]
+    lib.qsa_flash_attend.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_int64, P]
     lib.qsa_flash_workspace_bytes.argtypes = [SP]
     lib.qsa_flash_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_merge.argtypes = [SP, P, P, P]
@@ -103,7 +107,8 @@ def load_library(path: str = LIB_PATH):
     lib.qsa_status_string.restype = ctypes.c_char_p
     lib.qsa_part_elems.argtypes = [SP]
     lib.qsa_part_elems.restype = ctypes.c_int64
-    for f in (lib.qsa_topk, lib.qsa_flash, lib.qsa_merge):
+    for f in (lib.qsa_topk, lib.qsa_flash, lib.qsa_flash_prepare, lib.qsa_flash_attend,
+              lib.qsa_merge):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -205,6 +210,52 @@ def qsa_flash(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None, workspa
     rc = load_library().qsa_flash(ctypes.byref(cs), *args, ws_ptr, ws_bytes, _stream(stream))
     if rc != QSA_OK:
         raise QsaError(rc, "qsa_flash")
+
+
+def _kv_args(s: QsaShape, kq, ksc, vq, vsc) -> list:
+    import torch
+    G, N, D = s.n_groups, s.n_cells, s.head_dim
+    return [_dev_ptr(kq, "kq", torch.int8, (G, N, D)),
+            _dev_ptr(ksc, "ksc", torch.float16, (G, N, D // 64)),
+            _dev_ptr(vq, "vq", torch.int8, (G, N, D)),
+            _dev_ptr(vsc, "vsc", torch.float16, (G, N, D // 64))]
+
+
+def _ws_args(s: QsaShape, workspace, device) -> list:
+    import torch
+    if workspace is None:
+        workspace = flash_workspace(s, device)
+    if workspace is None:
+        return [None, 0]
+    return [_dev_ptr(workspace, "workspace", torch.uint8), workspace.numel()]
+
+
+def qsa_flash_prepare(shape: QsaShape, kq, ksc, vq, vsc, workspace=None, stream=None) -> None:
+    """First half of a fused qsa_flash call: dequantise the cells shared by
+    the tokens under budget into ``workspace`` (nothing when there are none)."""
+    s = shape
+    cs = s.c()
+    rc = load_library().qsa_flash_prepare(ctypes.byref(cs), *_kv_args(s, kq, ksc, vq, vsc),
+                                          *_ws_args(s, workspace, kq.device), _stream(stream))
+    if rc != QSA_OK:
+        raise QsaError(rc, "qsa_flash_prepare")
+
+
+def qsa_flash_attend(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, workspace=None,
+                     stream=None) -> None:
+    """Second half of a fused qsa_flash call: attention of every token, from a
+    workspace filled by qsa_flash_prepare (same shape and K/V) on this stream."""
+    import torch
+    s = shape
+    H, D = s.n_heads, s.head_dim
+    args = ([_dev_ptr(q, "q", torch.float16, (s.T, H, D))] + _kv_args(s, kq, ksc, vq, vsc) +
+            [_dev_ptr(ids, "ids", torch.int32, (s.T, s.n_groups, s.budget)),
+             _dev_ptr(out, "out", torch.float16, (s.T, H, D))])
+    cs = s.c()
+    rc = load_library().qsa_flash_attend(ctypes.byref(cs), *args,
+                                         *_ws_args(s, workspace, q.device), _stream(stream))
+    if rc != QSA_OK:
+        raise QsaError(rc, "qsa_flash_attend")
 
 
 def qsa_merge(shape: QsaShape, part, out, stream=None) -> None:

@@ -76,50 +76,104 @@ int64_t qsa_flash_workspace_bytes(const qsa_shape* s) {
   return qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host-side checks and argument packing shared by the qsa_flash entry points.
+int flash_args(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
+               const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+               float* part, qsa::RowArgs* a) {
+  int rc = check_shape(s);
+  if (rc != QSA_OK) return rc;
+  if (!kq || !ksc || !vq || !vsc) return QSA_ERR_ARG;
+  if (!aligned(kq, 16) || !aligned(vq, 16) || !aligned(ksc, 8) || !aligned(vsc, 8))
+    return QSA_ERR_ARG;
+  a->q = q;
+  a->kq = kq;
+  a->ksc = ksc;
+  a->vq = vq;
+  a->vsc = vsc;
+  a->ids = ids;
+  a->out = out;
+  a->part = part;
+  a->T = s->T;
+  a->pos0 = s->pos0;
+  a->G = s->n_groups;
+  a->budget = s->budget;
+  a->KC = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
+  a->n_items = 0;
+  a->n_cells = s->n_cells;
+  return QSA_OK;
+}
+
+// The fused path's workspace: needed for the identity prefix only.
+int check_workspace(const qsa_shape* s, const void* workspace, int64_t workspace_bytes) {
+  const int64_t need = qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+  if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need))
+    return QSA_ERR_ARG;
+  return QSA_OK;
+}
+
+// q, ids and out of a fused call (attention half).
+int check_attend(const qsa_shape* s, const _Float16* q, const int32_t* ids, const _Float16* out) {
+  if (!q || !aligned(q, 16)) return QSA_ERR_ARG;
+  if (any_above_budget(s) && (!ids || !aligned(ids, 4))) return QSA_ERR_ARG;
+  if (!out || !aligned(out, 16)) return QSA_ERR_ARG;
+  return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_flash_prepare(const qsa_shape* s, const int8_t* kq, const _Float16* ksc,
+                      const int8_t* vq, const _Float16* vsc, void* workspace,
+                      int64_t workspace_bytes, void* stream) {
+  qsa::RowArgs a;
+  int rc = flash_args(s, nullptr, kq, ksc, vq, vsc, nullptr, nullptr, nullptr, &a);
+  if (rc == QSA_OK) rc = check_workspace(s, workspace, workspace_bytes);
+  if (rc != QSA_OK) return rc;
+  return launch_status(
+      qsa::launch_tile_prepare(a, identity_tokens(s), workspace, (hipStream_t)stream));
+}
+
+int qsa_flash_attend(const qsa_shape* s, const _Float16* q, const int8_t* kq,
+                     const _Float16* ksc, const int8_t* vq, const _Float16* vsc,
+                     const int32_t* ids, _Float16* out, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  qsa::RowArgs a;
+  int rc = flash_args(s, q, kq, ksc, vq, vsc, ids, out, nullptr, &a);
+  if (rc == QSA_OK) rc = check_attend(s, q, ids, out);
+  if (rc == QSA_OK) rc = check_workspace(s, workspace, workspace_bytes);
+  if (rc != QSA_OK) return rc;
+  // tokens under budget (a prefix of the chunk) see a common prefix of
+  // cells, dequantised once into the workspace and shared by the tiled
+  // kernel; tokens above budget gather their own ids row by row
+  const int t_id = identity_tokens(s);
+  hipStream_t st = (hipStream_t)stream;
+  rc = launch_status(qsa::launch_tile_attend(a, t_id, workspace, st));
+  if (rc != QSA_OK) return rc;
+  return launch_status(qsa::launch_flash_rows(a, false, t_id, st));
+}
+
 int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
               const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
               float* part, void* workspace, int64_t workspace_bytes, void* stream) {
-  int rc = check_shape(s);
-  if (rc != QSA_OK) return rc;
-  if (!q || !kq || !ksc || !vq || !vsc) return QSA_ERR_ARG;
-  if (!aligned(q, 16) || !aligned(kq, 16) || !aligned(vq, 16) || !aligned(ksc, 8) ||
-      !aligned(vsc, 8))
-    return QSA_ERR_ARG;
-  if (any_above_budget(s) && (!ids || !aligned(ids, 4))) return QSA_ERR_ARG;
-  const bool split = part != nullptr;
-  if (split) {
-    if (!aligned(part, 16)) return QSA_ERR_ARG;
-  } else {
-    if (!out || !aligned(out, 16)) return QSA_ERR_ARG;
-  }
   qsa::RowArgs a;
-  a.q = q;
-  a.kq = kq;
-  a.ksc = ksc;
-  a.vq = vq;
-  a.vsc = vsc;
-  a.ids = ids;
-  a.out = out;
-  a.part = part;
-  a.T = s->T;
-  a.pos0 = s->pos0;
-  a.G = s->n_groups;
-  a.budget = s->budget;
-  a.KC = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
-  a.n_items = 0;
-  a.n_cells = s->n_cells;
-  hipStream_t st = (hipStream_t)stream;
-  if (split) return launch_status(qsa::launch_flash_rows(a, true, 0, st));
-  // fused: tokens under budget (a prefix of the chunk) see a common prefix
-  // of cells, dequantised once into the workspace and shared by the tiled
-  // kernel; tokens above budget gather their own ids row by row
-  const int t_id = identity_tokens(s);
-  const int64_t need = qsa::tile_workspace_bytes(s->n_groups, t_id, s->pos0);
-  if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need))
-    return QSA_ERR_ARG;
-  rc = launch_status(qsa::launch_flash_tile(a, t_id, workspace, st));
+  int rc = flash_args(s, q, kq, ksc, vq, vsc, ids, out, part, &a);
   if (rc != QSA_OK) return rc;
-  return launch_status(qsa::launch_flash_rows(a, false, t_id, st));
+  if (part) {  // split mode: per-chunk partial records, every row by the row kernel
+    if (!q || !aligned(q, 16) || !aligned(part, 16)) return QSA_ERR_ARG;
+    if (any_above_budget(s) && (!ids || !aligned(ids, 4))) return QSA_ERR_ARG;
+    return launch_status(qsa::launch_flash_rows(a, true, 0, (hipStream_t)stream));
+  }
+  rc = check_attend(s, q, ids, out);
+  if (rc == QSA_OK) rc = check_workspace(s, workspace, workspace_bytes);
+  if (rc != QSA_OK) return rc;
+  rc = qsa_flash_prepare(s, kq, ksc, vq, vsc, workspace, workspace_bytes, stream);
+  if (rc != QSA_OK) return rc;
+  return qsa_flash_attend(s, q, kq, ksc, vq, vsc, ids, out, workspace, workspace_bytes, stream);
 }
 
 int qsa_merge(const qsa_shape* s, const float* part, _Float16* out, void* stream) {

@@ -388,106 +388,97 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       }
     };
     // The same chunk for the fast pass, as an explicit schedule of stages
-    // of four MFMAs: the operand fragments of stage i + 2 are read while
-    // stage i multiplies, the softmax exponentials of chunk c are spread
+    // of four MFMAs: the operand fragments of stage i + kAhead are read
+    // while stage i multiplies, the softmax exponentials of chunk c are spread
     // over the score stages, and scheduler fences keep that order.
-    auto step_fast = [&](int c, auto NEXT_T, auto P_T) {
-      constexpr bool NEXT = decltype(NEXT_T)::value;
-      constexpr int P = decltype(P_T)::value;
-      constexpr int kS = NEXT ? 8 : 0;  // score stages (k-steps of chunk c + 1)
-      constexpr int kStages = kS + 8;   // then PV stages: k-step t / 4, m-tiles 4 (t % 4) ..
+    // Every chunk runs the same body, so the buffer parity is a run-time
+    // offset and the last chunk's score stages multiply a stale K image (in
+    // bounds, untouched by copies) whose result is dropped.
+    auto step_fast = [&](int c) {
+      constexpr int kS = 8;            // score stages (k-steps of chunk c + 1)
+      constexpr int kStages = kS + 8;  // then PV stages: k-step t / 4, m-tiles 4 (t % 4) ..
+      constexpr int kAhead = 1;        // stages whose fragments are read ahead
+      const uint32_t kpar = ((c + 1) & 1) * kHalf, vpar = (c & 1) * kHalf;
       wait_vmcnt0();  // this wave's copies of K(c+1) and V(c) have landed
       wg_barrier();   // ... every wave's; and nobody reads K(c) or V(c-1) any more
       if (c + 2 < nch) copy_k(c + 2);
       if (c + 1 < nch) copy_v(c + 1);
       mask(c, s_cur);
-      half8_t fr[3][4];
+      half8_t fr[kAhead + 1][4];
       auto load = [&](auto I, half8_t (&dst)[4]) {
         constexpr int i = decltype(I)::value;
         if constexpr (i < kS) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-            dst[mt] = lds16(koff[i & 3] +
-                            ((1 - P) * kHalf + 256 * (i >> 2) + mt * 16 * (kHeadDim * 2)));
+            dst[mt] = lds16(koff[i & 3] + kpar + (256 * (i >> 2) + mt * 16 * (kHeadDim * 2)));
         } else {
           constexpr int t = i - kS;
 #pragma unroll
           for (int m = 0; m < 4; ++m)
-            dst[m] = lds16(voff[t >> 2] + (P * kHalf + (4 * (t & 3) + m) * 16 * (kChunk * 2)));
+            dst[m] = lds16(voff[t >> 2] + vpar + ((4 * (t & 3) + m) * 16 * (kChunk * 2)));
         }
       };
       f32x4 s_nxt[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) s_nxt[mt] = zero4();
-      load(std::integral_constant<int, 0>{}, fr[0]);
-      load(std::integral_constant<int, 1>{}, fr[1]);
+      static_for<kAhead>([&](auto I) { load(I, fr[decltype(I)::value]); });
       const float cm = chunk_max(s_cur);
       m_ref = c == 0 ? cm : m_ref;  // chunk 0 always holds cell 0: finite
       over |= qvalid && cm > m_ref + kMaxGrowth;
       const float nm = -m_ref;
-      float p[16];  // exponentials in B-operand slot order: 8 kk + e
-      half8_t pb[2];
-      auto expo = [&](int q) {
-        const int kk = q >> 3, e = q & 7;
-        p[q] = fast_exp2(__builtin_fmaf(s_cur[2 * kk + (e >> 2)][e & 3], kScoreScaleLog2, nm));
+      half8_t pb[2];  // P in B-operand slot order: k-step kk, slot e
+      // exponentials of slots 2 i and 2 i + 1 (slot q = 8 kk + e), rounded
+      // to fp16 at once; l sums the fp32 values
+      auto expo2 = [&](int i) {
+        const int kk = i >> 2, e = 2 * (i & 3);
+        const float p0 =
+            fast_exp2(__builtin_fmaf(s_cur[2 * kk + (e >> 2)][e & 3], kScoreScaleLog2, nm));
+        const float p1 =
+            fast_exp2(__builtin_fmaf(s_cur[2 * kk + (e >> 2)][(e & 3) + 1], kScoreScaleLog2, nm));
+        pb[kk][e] = (_Float16)p0;
+        pb[kk][e + 1] = (_Float16)p1;
+        l_run += p0 + p1;
       };
-      auto pack = [&](int kk) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kk][e] = (_Float16)p[8 * kk + e];
-        l_run += ((p[8 * kk] + p[8 * kk + 1]) + (p[8 * kk + 2] + p[8 * kk + 3])) +
-                 ((p[8 * kk + 4] + p[8 * kk + 5]) + (p[8 * kk + 6] + p[8 * kk + 7]));
-      };
-      if constexpr (!NEXT) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) expo(q);
-        pack(0);
-      }
       __builtin_amdgcn_sched_barrier(0);
       static_for<kStages>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        if constexpr (i + 2 < kStages) load(std::integral_constant<int, i + 2>{}, fr[(i + 2) % 3]);
+        if constexpr (i + kAhead < kStages)
+          load(std::integral_constant<int, i + kAhead>{}, fr[(i + kAhead) % (kAhead + 1)]);
         if constexpr (i < kS) {
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) s_nxt[mt] = mfma16(fr[i % 3][mt], qf[i], s_nxt[mt]);
-          expo(2 * i);
-          expo(2 * i + 1);
-          if constexpr (i == 3) pack(0);
-          if constexpr (i == 7) pack(1);
+          for (int mt = 0; mt < 4; ++mt)
+            s_nxt[mt] = mfma16(fr[i % (kAhead + 1)][mt], qf[i], s_nxt[mt]);
+          expo2(i);
         } else {
           constexpr int t = i - kS;
 #pragma unroll
           for (int m = 0; m < 4; ++m)
-            oacc[4 * (t & 3) + m] = mfma16(fr[i % 3][m], pb[t >> 2], oacc[4 * (t & 3) + m]);
-          if constexpr (!NEXT && t < 4) {
-            expo(8 + 2 * t);
-            expo(9 + 2 * t);
-            if constexpr (t == 3) pack(1);
-          }
+            oacc[4 * (t & 3) + m] =
+                mfma16(fr[i % (kAhead + 1)][m], pb[t >> 2], oacc[4 * (t & 3) + m]);
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-      if constexpr (NEXT) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) s_cur[mt] = s_nxt[mt];
-      }
+      for (int mt = 0; mt < 4; ++mt) s_cur[mt] = s_nxt[mt];
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    auto any_step = [&](int c, auto NEXT_T, auto P_T) {
-      if constexpr (SAFE) step(c, NEXT_T, P_T); else step_fast(c, NEXT_T, P_T);
-    };
-    int c = 0;
-    for (; c + 2 < nch; c += 2) {
-      any_step(c, T_{}, P0{});
-      any_step(c + 1, T_{}, P1{});
-    }
-    if (c + 1 < nch) {
-      any_step(c, T_{}, P0{});
-      any_step(c + 1, F_{}, P1{});
+    if constexpr (SAFE) {
+      int c = 0;
+      for (; c + 2 < nch; c += 2) {
+        step(c, T_{}, P0{});
+        step(c + 1, T_{}, P1{});
+      }
+      if (c + 1 < nch) {
+        step(c, T_{}, P0{});
+        step(c + 1, F_{}, P1{});
+      } else {
+        step(c, F_{}, P0{});
+      }
     } else {
-      any_step(c, F_{}, P0{});
+      for (int c = 0; c < nch; ++c) step_fast(c);
     }
 
     if constexpr (!SAFE) {
@@ -530,18 +521,22 @@ int64_t tile_workspace_bytes(int G, int t_count, int pos0) {
   return (int64_t)G * nchunks * kImg;
 }
 
-hipError_t launch_flash_tile(const RowArgs& a, int t_count, void* ws, hipStream_t stream) {
+hipError_t launch_tile_prepare(const RowArgs& a, int t_count, void* ws, hipStream_t stream) {
   if (t_count <= 0) return hipSuccess;
   const int n_needed = a.pos0 + t_count;
   const int nchunks = (n_needed + kChunk - 1) / kChunk;
-  uint8_t* img = static_cast<uint8_t*>(ws);
-  dequant_chunks_kernel<<<dim3(a.G * nchunks * 2), dim3(256), 0, stream>>>(a, n_needed, nchunks,
-                                                                           img);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  dequant_chunks_kernel<<<dim3(a.G * nchunks * 2), dim3(256), 0, stream>>>(
+      a, n_needed, nchunks, static_cast<uint8_t*>(ws));
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_attend(const RowArgs& a, int t_count, const void* ws, hipStream_t stream) {
+  if (t_count <= 0) return hipSuccess;
+  const int n_needed = a.pos0 + t_count;
+  const int nchunks = (n_needed + kChunk - 1) / kChunk;
   const int n_blocks = (t_count + kTileTokens - 1) / kTileTokens;
-  flash_tile_kernel<<<dim3(n_blocks * a.G), dim3(kWaves * 64), 0, stream>>>(a, t_count, nchunks,
-                                                                           img);
+  flash_tile_kernel<<<dim3(n_blocks * a.G), dim3(kWaves * 64), 0, stream>>>(
+      a, t_count, nchunks, static_cast<const uint8_t*>(ws));
   return hipGetLastError();
 }
 

@@ -27,10 +27,12 @@ hipError_t launch_merge(const float* part, _Float16* out, int T, int H, int pos0
 // Row kernel: one wavefront per (token, group) row for tokens [t_begin, T)
 // (fused), or per (token, group, chunk) for all tokens (split mode).
 hipError_t launch_flash_rows(const RowArgs& a, bool split, int t_begin, hipStream_t stream);
-// Tile path: fused attention of tokens [0, t_count), all under budget.  It
-// dequantises cells [0, pos0 + t_count) of every group into `ws` (which must
-// hold tile_workspace_bytes(G, t_count, pos0) bytes), then attends.
+// Tile path: fused attention of tokens [0, t_count), all under budget.
+// launch_tile_prepare dequantises cells [0, pos0 + t_count) of every group
+// into `ws` (which must hold tile_workspace_bytes(G, t_count, pos0) bytes);
+// launch_tile_attend then attends from it.
 int64_t tile_workspace_bytes(int G, int t_count, int pos0);
-hipError_t launch_flash_tile(const RowArgs& a, int t_count, void* ws, hipStream_t stream);
+hipError_t launch_tile_prepare(const RowArgs& a, int t_count, void* ws, hipStream_t stream);
+hipError_t launch_tile_attend(const RowArgs& a, int t_count, const void* ws, hipStream_t stream);
 
 }  // namespace qsa

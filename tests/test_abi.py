@@ -73,6 +73,11 @@ def test_missing_workspace_is_rejected():
     assert _raw(lib, "qsa_flash", s, A, A, A, A, A, 0, A, 0, 0, 0, None) == E
     assert _raw(lib, "qsa_flash", s, A, A, A, A, A, 0, A, 0, A, need - 1, None) == E
     assert _raw(lib, "qsa_flash", s, A, A, A, A, A, 0, A, 0, A + 16, need, None) == E
+    # the two halves of the fused path need the same workspace
+    assert _raw(lib, "qsa_flash_prepare", s, A, A, A, A, 0, 0, None) == E
+    assert _raw(lib, "qsa_flash_prepare", s, A, A, A, A, A, need - 1, None) == E
+    assert _raw(lib, "qsa_flash_attend", s, A, A, A, A, A, 0, A, 0, 0, None) == E
+    assert _raw(lib, "qsa_flash_attend", s, A, A, A, A, A, 0, A, A + 16, need, None) == E
 
 
 def test_part_elems_layout():
@@ -81,9 +86,13 @@ def test_part_elems_layout():
     assert qsa.qsa_part_elems(qsa.QsaShape(T=0, pos0=0)) == 0
 
 
+# position of the int64 workspace_bytes argument (after the shape) per entry point
+_SIZE_ARG = {"qsa_flash": 9, "qsa_flash_prepare": 5, "qsa_flash_attend": 8}
+
+
 def _raw(lib, fn, shape, *args):
     cs = shape.c()
-    conv = [a if isinstance(a, int) and fn == "qsa_flash" and i == 9 else
+    conv = [a if isinstance(a, int) and _SIZE_ARG.get(fn) == i else
             (ctypes.c_void_p(a) if a else None) for i, a in enumerate(args)]
     return getattr(lib, fn)(ctypes.byref(cs), *conv)
 
@@ -106,6 +115,9 @@ def test_bad_shapes_are_rejected(shape, expect):
                 None) == expect
     assert _raw(lib, "qsa_topk", s, fake, fake, None) == expect
     assert _raw(lib, "qsa_merge", s, fake, fake, None) == expect
+    assert _raw(lib, "qsa_flash_prepare", s, fake, fake, fake, fake, None, 0, None) == expect
+    assert _raw(lib, "qsa_flash_attend", s, fake, fake, fake, fake, fake, fake, fake, None, 0,
+                None) == expect
 
 
 def test_null_and_misaligned_pointers_are_rejected():
@@ -122,6 +134,11 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert _raw(lib, "qsa_flash", over, A, A, A, A, A, 0, A, 0, None, 0, None) == E        # ids needed
     assert _raw(lib, "qsa_flash", over, A, A, A, A, A, A + 2, A, 0, None, 0, None) == E    # ids 4 B
     assert _raw(lib, "qsa_flash", under, A, A, A, A, A, 0, 0, A + 8, None, 0, None) == E   # part 16 B
+    # attend: q, kq, ksc, vq, vsc, ids, out, workspace, workspace_bytes
+    assert _raw(lib, "qsa_flash_attend", over, 0, A, A, A, A, A, A, None, 0, None) == E  # q
+    assert _raw(lib, "qsa_flash_attend", over, A, A, A, A, A, 0, A, None, 0, None) == E  # ids
+    assert _raw(lib, "qsa_flash_attend", over, A, A, A, A, A, A, 0, None, 0, None) == E  # out
+    assert _raw(lib, "qsa_flash_prepare", under, A + 4, A, A, A, A, 1 << 30, None) == E  # kq
     assert _raw(lib, "qsa_topk", over, 0, A, None) == E                           # scores
     assert _raw(lib, "qsa_topk", under, 0, 0, None) == E                          # ids
     assert _raw(lib, "qsa_merge", under, A, A + 2, None) == E

@@ -179,3 +179,30 @@ def test_long_context_sampled_tokens():
         ids = oracle.select(1, sub.pos0, sub.budget, sub.scores, 2, sub.n_cells)
         np.testing.assert_array_equal(gids[t:t + 1], ids)
         _check(got[t:t + 1], oracle.attend(sub, ids))
+
+
+@pytest.mark.parametrize("T,pos0", [(96, 0), (96, 2050), (200, 1900)])
+def test_prepare_then_attend_equals_fused_call(T, pos0):
+    # the two halves of a fused qsa_flash call, enqueued separately, give the
+    # same bytes as the one call (and so the same oracle match)
+    import torch
+    import quantized_sparse_flash_amd as qsa
+    from gpu_util import shape_of
+    inp = qsa_synth.layer_inputs(T, pos0, seed=11)
+    ids = oracle.select(T, pos0, inp.budget, inp.scores, 2, inp.n_cells) \
+        if inp.scores is not None else None
+    dev = upload(inp)
+    fused = gpu_flash(inp, ids, dev)
+    s = shape_of(inp)
+    idt = None if ids is None else torch.from_numpy(np.ascontiguousarray(ids)).cuda()
+    out = torch.full((s.T, s.n_heads, s.head_dim), float("nan"), dtype=torch.float16,
+                     device="cuda")
+    ws = qsa.flash_workspace(s, out.device)
+    if ws is not None:
+        ws.fill_(0xFF)  # the prepare half must overwrite every byte the attend half reads
+    qsa.qsa_flash_prepare(s, dev["kq"], dev["ksc"], dev["vq"], dev["vsc"], ws)
+    qsa.qsa_flash_attend(s, dev["q"], dev["kq"], dev["ksc"], dev["vq"], dev["vsc"], idt, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(got, fused)
+    _check(got, oracle.attend(inp, ids))
