@@ -6,146 +6,382 @@
 // index semantics above budget are kept).  Tie rule and order (lower index
 // first on equal scores, ids ascending) are this library's reading.
 //
-// One workgroup of 1024 threads per row.  Identity rows are written
-// directly.  Above budget, an MSB-first radix select over order-preserving
-// 32-bit keys finds the budget-th largest key K (4 passes of 8-bit digits,
-// per-wave LDS histograms), then an ordered compaction writes, in ascending
-// index order, every cell with key > K and the lowest-index cells with
-// key == K until exactly `budget` ids are out.
+// One workgroup per row.  Identity rows are written directly.  Above budget
+// the row's scores become order-preserving 32-bit keys and an MSB-first
+// radix select finds K, the key of the budget-th largest score, and krem,
+// how many cells with key == K are taken (the lowest-index ones).  The
+// selected cells are then every key > K plus those krem, written in
+// ascending index order.
+//
+//   topk_regs_kernel (rows of at most 512 x 64 cells): the row is read from
+//     HBM once, coalesced, into registers (EPT keys per thread).  Three
+//     radix passes of 11, 11 and 10 bits count digits with LDS atomics; only
+//     the first pass touches every key, the later ones only keys that match
+//     the prefix found so far.  The selection is then two LDS bitmaps over
+//     the row's cells (key > K, key == K), built from one ballot per 64
+//     cells, and two block-wide scans over the bitmap words: the first keeps
+//     the first krem equal keys, the second gives every selected cell its
+//     output position.
+//
+//   topk_stream_kernel (longer rows): the same radix select with 8-bit
+//     digits, re-reading the row from memory in each of four passes, and an
+//     ordered ballot compaction.
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
 namespace qsa {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
+namespace {
 
-// Order-preserving key: larger float -> larger unsigned; -0.0 == +0.0.
+// Order-preserving key: larger float -> larger unsigned; -0.0 == +0.0
+// (x + 0 turns -0 into +0 under round-to-nearest; then negative values have
+// all bits flipped, positive ones only the sign bit).  NaN inputs are
+// unsupported; -inf maps to 0x007fffff, so key 0 is below every real score
+// and marks cells outside the row.
 __device__ __forceinline__ uint32_t score_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-struct TopkShared {
-  uint32_t hist[kTopkWaves][256];
-  uint32_t tot[256];
-  uint32_t wscan[kTopkWaves];
-  uint32_t wscan2[kTopkWaves];
-  uint32_t digit;
-  uint32_t above;   // keys in digits strictly above the chosen one
-  uint32_t in_dig;  // keys in the chosen digit
-};
+// Inclusive prefix sum over the 64 lanes of a wave on DPP: shifts by 1, 2,
+// 4 and 8 lanes inside each 16-lane row, then row_bcast:15 / row_bcast:31
+// carry row totals into the rows above (gfx9-family DPP controls; lanes
+// without a source add the 0 passed as `old`).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
 
-// Exclusive prefix of `flag` over the block in thread order; returns the
-// thread's offset and writes the block total.  Two barriers.
-__device__ __forceinline__ uint32_t block_excl_scan(bool flag, uint32_t* wsc, uint32_t& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint64_t m = __ballot(flag);
-  const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) wsc[w] = __popcll(m);
+// Exclusive prefix sum of v over a block of NT threads in thread order;
+// writes the block total.  `wsum` holds NT / 64 words; two barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int w = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_sum(v);
+  if ((threadIdx.x & 63) == 63) wsum[w] = incl;
   __syncthreads();
-  uint32_t off = 0, tot = 0;
+  uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kTopkWaves; ++i) {
-    const uint32_t c = wsc[i];
-    off += (i < w) ? c : 0u;
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t c = wsum[i];
+    base += (i < w) ? c : 0u;
     tot += c;
   }
   __syncthreads();
   total = tot;
-  return off + before;
+  return base + incl - v;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
-                                                            int32_t* __restrict__ ids, int T,
-                                                            int pos0, int G, int budget,
-                                                            int64_t n_cells) {
-  __shared__ TopkShared sh;
-  const int row = blockIdx.x;  // t * G + g
-  const int t = row / G;
-  const int64_t n = (int64_t)pos0 + t + 1;
-  int32_t* out = ids + (int64_t)row * budget;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// Buffer-resource word 3 for raw 32-bit loads on gfx9-family parts: the
+// hardware range check then returns 0 for offsets at or past the size.
+constexpr int kBufferFlags = 0x00020000;
 
+// Identity row: 0 .. n-1, then -1 padding.
+__device__ __forceinline__ void write_identity(int32_t* out, int64_t n, int budget, int nt) {
+  for (int i = threadIdx.x; i < budget; i += nt) out[i] = (i < n) ? i : -1;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ register rows
+constexpr int kRegThreads = 512;
+constexpr int kRegMaxEpt = 64;    // keys per thread: rows up to 32,768 cells
+constexpr int kListCap = 6144;    // survivors of the first digit kept in LDS
+
+template <int EPT>
+__global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+topk_regs_kernel(const float* __restrict__ scores,
+                                                                int32_t* __restrict__ ids, int G,
+                                                                int pos0, int budget,
+                                                                int64_t n_cells) {
+  constexpr int NT = kRegThreads, NW = NT / 64;
+  constexpr int kWords = NT * EPT / 32;         // bitmap words per row
+  constexpr int kWpt = (kWords + NT - 1) / NT;  // words per thread
+  // hist[0] serves every pass; in the first pass hist[1..3] are extra copies
+  // (one per 16-lane quarter of a wave, fewer same-bin atomic collisions),
+  // afterwards their space holds the survivors of the first digit
+  __shared__ uint32_t hist[4][2048];
+  uint32_t* const list = &hist[1][0];
+  static_assert(3 * 2048 >= kListCap, "survivor list fits in hist[1..3]");
+  __shared__ __attribute__((aligned(8))) uint32_t bm_gt[kWords], bm_eq[kWords];  // key > K (or >=), == K
+  __shared__ uint32_t wsum[NW], wcount[NW];
+  __shared__ uint32_t s_digit, s_above, s_count;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int row = blockIdx.x;  // t * G + g
+  const int64_t n = (int64_t)pos0 + row / G + 1;
+  int32_t* out = ids + (int64_t)row * budget;
   if (n <= budget) {
-    for (int i = tid; i < budget; i += kTopkThreads) out[i] = (i < n) ? i : -1;
+    write_identity(out, n, budget, NT);
+    return;
+  }
+
+  // ---- cell tid + NT i of the row -> key[i] (0 past the row's end).  Raw
+  // buffer loads: slice i (cells NT i ..) gets a resource of its own, built
+  // on the scalar unit, whose size stops at the row's end, so the hardware
+  // range check returns 0 past it; every load is unconditional (all in
+  // flight at once) and uses the one lane offset 4 tid.
+  const int n32 = (int)n;  // <= NT * EPT
+  const float* srow = scores + (int64_t)row * n_cells;
+  uint32_t key[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int start = min(NT * i, n32);  // at most one past the row's end
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(srow + start), (short)0, 4 * (n32 - start), kBufferFlags);
+    key[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 0, 0);
+    // fence every 8 loads: the scheduler would otherwise hoist all EPT
+    // resources (4 scalar registers each) ahead of the loads
+    if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- radix select, most significant digit first.  The block finds the
+  // digit of the krem-th largest remaining key from a histogram `h`.
+  uint32_t prefix = 0, krem = (uint32_t)budget, eq_count = 0;
+  auto choose = [&](int shift, bool four_copies) {
+    // bins in descending order: thread tid owns bins 2047 - 4 tid - q, q < 4
+    uint32_t c[4], mine = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = 2047 - 4 * tid - q;
+      c[q] = hist[0][b];
+      if (four_copies) c[q] += hist[1][b] + hist[2][b] + hist[3][b];
+      mine += c[q];
+    }
+    uint32_t total;
+    const uint32_t excl = block_excl_sum<NT>(mine, wsum, total);
+    if (excl < krem && krem <= excl + mine) {  // exactly one thread
+      uint32_t acc = excl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (acc < krem && krem <= acc + c[q]) {
+          s_digit = 2047u - 4u * tid - q;
+          s_above = acc;
+          s_count = c[q];
+        }
+        acc += c[q];
+      }
+    }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    krem -= s_above;
+    eq_count = s_count;
+    __syncthreads();  // everyone has read s_* before they are rewritten
+  };
+  auto clear_hist = [&](int words) {
+    for (int b = tid; b < words; b += NT) (&hist[0][0])[b] = 0u;
+    __syncthreads();
+  };
+
+  // first digit: bits 31..21 of every key, counted as the loads land (each
+  // key is converted, then counted; fences every 8 keys keep the scheduler
+  // from computing all bin addresses at once)
+  clear_hist(4 * 2048);
+  {
+    uint32_t* h = hist[lane >> 4];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      key[i] = score_key(__builtin_bit_cast(float, key[i]));
+      if (NT * (i + 1) > n32)  // slice reaches past the row's end (a scalar test)
+        key[i] = tid < n32 - NT * i ? key[i] : 0u;
+      atomicAdd(&h[key[i] >> 21], 1u);
+      if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+  choose(21, true);
+  const uint32_t d1 = prefix >> 21;
+  const uint32_t n1 = eq_count;  // keys whose first digit is d1 (they hold the answer)
+
+  if (n1 <= (uint32_t)kListCap) {
+    // survivors of the first digit -> list, wave by wave in cell order
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) cnt += __popcll(__ballot((key[i] >> 21) == d1));
+    if (lane == 0) wcount[w] = cnt;
+    clear_hist(2048);  // (its barrier also publishes wcount)
+    uint32_t pos = 0;
+    for (int v = 0; v < w; ++v) pos += wcount[v];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const bool hit = (key[i] >> 21) == d1;
+      const uint64_t m = __ballot(hit);
+      if (hit) list[pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+          key[i];
+      pos += __popcll(m);
+    }
+    __syncthreads();
+    // second digit (bits 20..10) and third (bits 9..0) over the list
+    for (int j = tid; j < (int)n1; j += NT) atomicAdd(&hist[0][(list[j] >> 10) & 0x7ffu], 1u);
+    __syncthreads();
+    choose(10, false);
+    clear_hist(2048);
+    for (int j = tid; j < (int)n1; j += NT) {
+      const uint32_t k = list[j];
+      if ((k >> 10) == (prefix >> 10)) atomicAdd(&hist[0][k & 0x3ffu], 1u);
+    }
+    __syncthreads();
+    choose(0, false);
+  } else {
+    // too many survivors for the list: the same two digits over the registers
+    clear_hist(2048);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      if ((key[i] >> 21) == d1) atomicAdd(&hist[0][(key[i] >> 10) & 0x7ffu], 1u);
+    __syncthreads();
+    choose(10, false);
+    clear_hist(2048);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      if ((key[i] >> 10) == (prefix >> 10)) atomicAdd(&hist[0][key[i] & 0x3ffu], 1u);
+    __syncthreads();
+    choose(0, false);
+  }
+  const uint32_t K = prefix;  // krem (1 <= krem <= eq_count) cells with key K are taken
+
+  // ---- bitmaps: element row i of wave w covers cells [NT i + 64 w, +64)
+  // and its ballot is one 64-bit bitmap entry, stored by lane 0.  When every
+  // cell with key K is taken (the usual case) one bitmap of key >= K is the
+  // selection; otherwise key > K and key == K apart.
+  const bool take_all_eq = eq_count == krem;
+  uint64_t* const gt64 = reinterpret_cast<uint64_t*>(bm_gt);
+  uint64_t* const eq64 = reinterpret_cast<uint64_t*>(bm_eq);
+  if (take_all_eq) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const uint64_t g = __ballot(key[i] >= K);
+      if (lane == 0) gt64[(NT * i + 64 * w) >> 6] = g;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const uint64_t g = __ballot(key[i] > K);
+      const uint64_t e = __ballot(key[i] == K);
+      if (lane == 0) {
+        gt64[(NT * i + 64 * w) >> 6] = g;
+        eq64[(NT * i + 64 * w) >> 6] = e;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- thread tid owns bitmap words [kWpt tid, kWpt tid + kWpt) (index order)
+  uint32_t sel[kWpt];
+#pragma unroll
+  for (int k = 0; k < kWpt; ++k) {
+    const int wd = kWpt * tid + k;
+    sel[k] = wd < kWords ? bm_gt[wd] : 0u;
+  }
+  if (!take_all_eq) {  // ties at K: only the first krem of them, in index order
+    uint32_t n_eq = 0;
+#pragma unroll
+    for (int k = 0; k < kWpt; ++k) {
+      const int wd = kWpt * tid + k;
+      n_eq += wd < kWords ? __popc(bm_eq[wd]) : 0u;
+    }
+    uint32_t eq_total;
+    uint32_t rank = block_excl_sum<NT>(n_eq, wsum, eq_total);
+#pragma unroll
+    for (int k = 0; k < kWpt; ++k) {
+      const int wd = kWpt * tid + k;
+      uint32_t e = wd < kWords ? bm_eq[wd] : 0u;
+      while (e) {
+        const uint32_t bit = e & (0u - e);
+        if (rank < krem) sel[k] |= bit;
+        ++rank;
+        e ^= bit;
+      }
+    }
+  }
+  uint32_t n_sel = 0;
+#pragma unroll
+  for (int k = 0; k < kWpt; ++k) n_sel += __popc(sel[k]);
+  uint32_t sel_total;
+  uint32_t pos = block_excl_sum<NT>(n_sel, wsum, sel_total);  // sel_total == budget
+#pragma unroll
+  for (int k = 0; k < kWpt; ++k) {
+    uint32_t b = sel[k];
+    const int base = 32 * (kWpt * tid + k);
+    while (b) {
+      const int bit = __builtin_ctz(b);
+      if (pos < (uint32_t)budget) out[pos] = base + bit;  // exactly budget by construction
+      ++pos;
+      b &= b - 1u;
+    }
+  }
+}
+
+// ------------------------------------------------------------- streamed rows
+constexpr int kStreamThreads = 1024;
+constexpr int kStreamWaves = kStreamThreads / 64;
+
+__global__ __launch_bounds__(kStreamThreads) void topk_stream_kernel(
+    const float* __restrict__ scores, int32_t* __restrict__ ids, int G, int pos0, int budget,
+    int64_t n_cells) {
+  __shared__ uint32_t hist[kStreamWaves][256];
+  __shared__ uint32_t wsum[kStreamWaves];
+  __shared__ uint32_t s_digit, s_above, s_count;
+  const int row = blockIdx.x;
+  const int64_t n = (int64_t)pos0 + row / G + 1;
+  int32_t* out = ids + (int64_t)row * budget;
+  const int tid = threadIdx.x, w = tid >> 6;
+  if (n <= budget) {
+    write_identity(out, n, budget, kStreamThreads);
     return;
   }
   const float* s = scores + (int64_t)row * n_cells;
 
-  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)budget, eq_total = 0;
+  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)budget, eq_count = 0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
+    for (int i = tid; i < kStreamWaves * 256; i += kStreamThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kTopkThreads) {
+    for (int64_t i = tid; i < n; i += kStreamThreads) {
       const uint32_t key = score_key(s[i]);
-      if ((key & pmask) == prefix) atomicAdd(&sh.hist[w][(key >> shift) & 255u], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
     }
     __syncthreads();
+    uint32_t c = 0;
     if (tid < 256) {
-      uint32_t c = 0;
 #pragma unroll
-      for (int i = 0; i < kTopkWaves; ++i) c += sh.hist[i][tid];
-      sh.tot[tid] = c;
+      for (int i = 0; i < kStreamWaves; ++i) c += hist[i][255 - tid];  // descending digits
+    }
+    uint32_t total;
+    const uint32_t excl = block_excl_sum<kStreamThreads>(tid < 256 ? c : 0u, wsum, total);
+    if (tid < 256 && excl < krem && krem <= excl + c) {
+      s_digit = 255u - tid;
+      s_above = excl;
+      s_count = c;
     }
     __syncthreads();
-    // digit d* with  above(d*) < krem <= above(d*) + tot[d*], scanning from
-    // the top digit: inclusive prefix over reversed bins (first 4 waves)
-    // (tid < 256 selects whole waves 0..3, so the shuffles stay wave-uniform)
-    uint32_t c = 0, incl = 0;
-    if (tid < 256) {
-      c = sh.tot[255 - tid];
-      incl = c;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-      }
-      if (lane == 63) sh.wscan[w] = incl;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t base = 0;
-      for (int i = 0; i < w; ++i) base += sh.wscan[i];
-      incl += base;
-      const uint32_t excl = incl - c;
-      if (excl < krem && krem <= incl) {
-        sh.digit = 255u - tid;
-        sh.above = excl;
-        sh.in_dig = c;
-      }
-    }
-    __syncthreads();
-    const uint32_t d = sh.digit;
-    krem -= sh.above;
-    eq_total = sh.in_dig;
-    prefix |= d << shift;
+    prefix |= s_digit << shift;
     pmask |= 255u << shift;
+    krem -= s_above;
+    eq_count = s_count;
     __syncthreads();
   }
-  // prefix is the key K of the budget-th largest score; krem (>= 1) cells
-  // with key == K are taken, lowest index first; eq_total cells have key K.
   const uint32_t K = prefix;
-  const bool all_eq = (eq_total == krem);
+  const bool all_eq = eq_count == krem;
   uint32_t sel_base = 0, eq_base = 0;
-  for (int64_t base = 0; base < n; base += kTopkThreads) {
+  for (int64_t base = 0; base < n; base += kStreamThreads) {
     const int64_t i = base + tid;
-    uint32_t key = 0;
-    if (i < n) key = score_key(s[i]);
-    const bool gt = (i < n) && key > K;
-    const bool eq = (i < n) && key == K;
-    bool sel;
-    if (all_eq) {
-      sel = gt || eq;
-    } else {
-      uint32_t eq_round = 0;
-      const uint32_t eq_rank = eq_base + block_excl_scan(eq, sh.wscan, eq_round);
+    const uint32_t key = i < n ? score_key(s[i]) : 0u;
+    const bool gt = i < n && key > K;
+    const bool eq = i < n && key == K;
+    bool sel = gt || (all_eq && eq);
+    if (!all_eq) {
+      uint32_t eq_round;
+      const uint32_t eq_rank = eq_base + block_excl_sum<kStreamThreads>(eq, wsum, eq_round);
       eq_base += eq_round;
       sel = gt || (eq && eq_rank < krem);
     }
-    uint32_t sel_round = 0;
-    const uint32_t pos = sel_base + block_excl_scan(sel, sh.wscan2, sel_round);
+    uint32_t sel_round;
+    const uint32_t pos = sel_base + block_excl_sum<kStreamThreads>(sel, wsum, sel_round);
     sel_base += sel_round;
     if (sel && pos < (uint32_t)budget) out[pos] = (int32_t)i;  // exactly budget by construction
   }
@@ -153,8 +389,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 
 hipError_t launch_topk(const float* scores, int32_t* ids, int T, int pos0, int G, int budget,
                        int64_t n_cells, hipStream_t stream) {
-  dim3 grid(T * G), block(kTopkThreads);
-  topk_kernel<<<grid, block, 0, stream>>>(scores, ids, T, pos0, G, budget, n_cells);
+  const dim3 grid(T * G);
+  const int64_t n_max = (int64_t)pos0 + T;  // longest row
+  const int64_t per = (n_max + kRegThreads - 1) / kRegThreads;
+  if (per <= 8) {
+    topk_regs_kernel<8><<<grid, kRegThreads, 0, stream>>>(scores, ids, G, pos0, budget, n_cells);
+  } else if (per <= 16) {
+    topk_regs_kernel<16><<<grid, kRegThreads, 0, stream>>>(scores, ids, G, pos0, budget, n_cells);
+  } else if (per <= 32) {
+    topk_regs_kernel<32><<<grid, kRegThreads, 0, stream>>>(scores, ids, G, pos0, budget, n_cells);
+  } else if (per <= kRegMaxEpt) {
+    topk_regs_kernel<kRegMaxEpt>
+        <<<grid, kRegThreads, 0, stream>>>(scores, ids, G, pos0, budget, n_cells);
+  } else {
+    topk_stream_kernel<<<grid, kStreamThreads, 0, stream>>>(scores, ids, G, pos0, budget,
+                                                           n_cells);
+  }
   return hipGetLastError();
 }
 

@@ -66,3 +66,22 @@ def test_topk_long_context_sampled_rows():
     for t in sorted(set([0, 1983] + rng.integers(0, 1984, 14).tolist())):
         ref = oracle.select(1, 30000 + t, 2051, inp.scores[t:t + 1], 2, inp.n_cells)
         np.testing.assert_array_equal(ids[t:t + 1], ref)
+
+
+@pytest.mark.parametrize("kind", ["normal", "quantized"])
+def test_topk_rows_longer_than_the_register_tile(kind):
+    # rows of more than 512 x 64 cells take the streamed kernel: 3 tokens
+    # at pos0 33000 (up to 33,003 cells), normal and tie-heavy scores
+    T, pos0, B = 3, 33000, 2051
+    inp = _inputs_with_scores(T, pos0, B, kind, seed=17)
+    ref = oracle.select(T, pos0, B, inp.scores, 2, inp.n_cells)
+    np.testing.assert_array_equal(gpu_topk(inp), ref)
+
+
+@pytest.mark.parametrize("T,pos0", [(2, 32766), (2, 32767), (2, 16382), (2, 16383), (3, 4093)])
+def test_topk_rows_at_register_tile_edges(T, pos0):
+    # the longest row exactly fills (pos0 + T = 4096, 16384, 32768 cells) or
+    # just passes (16385, 32769) a register tile of 512 threads x 8/32/64
+    inp = _inputs_with_scores(T, pos0, 2051, "quantized", seed=pos0)
+    ref = oracle.select(T, pos0, 2051, inp.scores, 2, inp.n_cells)
+    np.testing.assert_array_equal(gpu_topk(inp), ref)
