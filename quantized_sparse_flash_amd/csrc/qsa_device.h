@@ -21,6 +21,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // S = 0.0625 * q.k, and the softmax runs in base 2: x = S * log2(e).
 constexpr float kScoreScaleLog2 = 0.0625f * kLog2e;
+// Buffer-resource word 3 for raw 32-bit loads on gfx9-family parts: the
+// hardware range check then returns 0 for offsets at or past the size.
+constexpr int kBufferFlags = 0x00020000;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));

@@ -17,7 +17,9 @@
 //     is 64*(s/2) + 16*j + 8*(s%2) + i, so one 16-byte load per scale block
 //     feeds two k-steps and each lane's codes share one K scale;
 //   * the softmax runs on the S^T accumulators: every lane holds one query
-//     and 16 cells, so row max/sum need only two cross-lane steps;
+//     and 16 cells, so row max/sum need only two cross-lane steps; the fused
+//     mode keeps a lazy reference max (O and l are rescaled only when a
+//     chunk max passes it by more than 2^8, so p stays below 2^8);
 //   * O^T[256 dims][16 queries] += V^T P^T: B = P^T comes straight from the
 //     S^T registers (the accumulator layout of two 16-cell tiles is exactly
 //     the B layout of one 32-cell k-step); A = V^T uses dim d = 16*r + mt for
@@ -32,6 +34,8 @@
 
 namespace qsa {
 
+constexpr float kLazyGrowth = 8.0f;  // log2 headroom of the running reference max
+
 
 __device__ __forceinline__ half2_t splat_lo(uint32_t u) {
   const half2_t h = as_h2(u);
@@ -43,10 +47,14 @@ __device__ __forceinline__ half2_t splat_hi(uint32_t u) {
 }
 
 
+// Two waves per SIMD (at most 256 registers each): the gathers are latency-
+// bound, and the second wave's loads overlap the first one's arithmetic.
 template <bool SPLIT>
-__global__ __launch_bounds__(256) void flash_rows_kernel(RowArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void flash_rows_kernel(RowArgs a) {
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform: every per-row value below lives in scalar registers
+  const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (item >= a.n_items) return;
   const int G = a.G, H = G * kHpg;
   int t, g, k_only = 0;
@@ -93,22 +101,25 @@ __global__ __launch_bounds__(256) void flash_rows_kernel(RowArgs a) {
   const int k_begin = SPLIT ? k_only : 0;
   const int k_end = SPLIT ? k_only + 1 : nch;
   float m_chunk = 0.f, l_chunk = 0.f;
+  // id of chunk position `lane`, fetched one chunk ahead and clamped when
+  // used; the row's ids sit behind a range-checked buffer (0 past the row)
+  const __amdgpu_buffer_rsrc_t ids_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(explicit_ids ? ids_row : a.ids), (short)0,
+      explicit_ids ? 4 * nsel : 0, kBufferFlags);
+  auto raw_id = [&](int k) -> int {
+    const int p = k * kChunk + lane;
+    if (!explicit_ids) return p < nsel ? p : 0;
+    return __builtin_amdgcn_raw_buffer_load_b32(ids_rs, 4 * p, 0, 0);
+  };
+  auto clamp_cell = [&](int c) -> int {
+    c = c < 0 ? 0 : c;
+    return (int64_t)c >= a.n_cells ? (int)(a.n_cells - 1) : c;
+  };
+  int next_raw = raw_id(k_begin);
   for (int k = k_begin; k < k_end; ++k) {
     const int cbase = k * kChunk;
-    // cell of chunk position `lane`
-    int my_cell = 0;
-    {
-      const int p = cbase + lane;
-      if (p < nsel) {
-        if (explicit_ids) {
-          int64_t c = ids_row[p];
-          c = c < 0 ? 0 : (c >= a.n_cells ? a.n_cells - 1 : c);
-          my_cell = (int)c;
-        } else {
-          my_cell = p;
-        }
-      }
-    }
+    const int my_cell = clamp_cell(next_raw);
+    next_raw = raw_id(k + 1);
 
     // ---- S^T = K Q^T, four 16-cell m-tiles
     f32x4 sacc[4];
@@ -154,12 +165,18 @@ __global__ __launch_bounds__(256) void flash_rows_kernel(RowArgs a) {
     if (SPLIT) {
       mref = cmax;
     } else {
-      mref = fmaxf(m_run, cmax);
-      const float alpha = fast_exp2(m_run - mref);
-      l_run *= alpha;
+      // the reference max moves only when a query's chunk max passes it by
+      // more than 2^kLazyGrowth; p may then exceed 1 by at most that factor
+      const bool grow = cmax > m_run + kLazyGrowth;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+        const float m_new = grow ? cmax : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 16; ++mt) oacc[mt] *= alpha;
-      m_run = mref;
+        for (int mt = 0; mt < 16; ++mt) oacc[mt] *= alpha;
+        m_run = m_new;
+      }
+      mref = m_run;
     }
     float lsum = 0.f;
     half8_t pb[2];

@@ -77,9 +77,6 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wsum, u
   return base + incl - v;
 }
 
-// Buffer-resource word 3 for raw 32-bit loads on gfx9-family parts: the
-// hardware range check then returns 0 for offsets at or past the size.
-constexpr int kBufferFlags = 0x00020000;
 
 // Identity row: 0 .. n-1, then -1 padding.
 __device__ __forceinline__ void write_identity(int32_t* out, int64_t n, int budget, int nt) {
