@@ -49,12 +49,12 @@
 //
 //     Softmax reference.  The first chunk sets each query's reference max
 //     exactly; later chunks keep it, so O is never rescaled.  P = 2^(x - m)
-//     then stays below 2^kMaxGrowth unless a later score exceeds the
-//     reference by more than that; lanes record whether one did, and the
-//     workgroup votes at the end.  After such a vote (rare) the block is
-//     recomputed by an exact online-softmax pass that moves the running max
-//     and rescales O.  Either way the result after the final division by l
-//     is the same softmax.
+//     may then exceed 1 when a later score passes the reference; every P is
+//     at most l (their fp32 sum), so l < 65504 at the end proves that no P
+//     overflowed fp16.  Otherwise (rare: scores far above chunk 0's) the
+//     workgroup votes to recompute the block by an exact online-softmax
+//     pass that moves the running max and rescales O.  Either way the result
+//     after the final division by l is the same softmax.
 //
 // Workgroup i takes KV group i % G; with G = 2 and workgroups dealt to the
 // 8 XCDs round robin, each XCD's L2 holds one group's images only.
@@ -71,7 +71,7 @@ constexpr int kWaves = 8;
 constexpr int kQpw = 16;                    // query slots per wave
 constexpr int kSlots = kQpw * kWaves;       // query slots per workgroup
 constexpr int kTileTokens = kSlots / kHpg;  // whole tokens per workgroup (10)
-constexpr float kMaxGrowth = 15.0f;         // log2 headroom above the reference max
+constexpr float kP16Max = 65504.0f;         // largest finite fp16
 constexpr int kHalf = kChunk * kHeadDim * 2;  // bytes of one K or V^T image (32 KB)
 constexpr int kImg = 2 * kHalf;               // bytes per (group, chunk) in the workspace
 constexpr int kCopyOps = kHalf / 1024 / kWaves;  // 1 KB copies per wave per image (4)
@@ -104,6 +104,17 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds) {
       "global_load_lds_dwordx4 %0, off"
       :
       : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory", "m0");
+}
+// The same copy from the wave-uniform base `base` plus the per-lane byte
+// offset `voff` (no immediate offset): no per-copy address math.
+__device__ __forceinline__ void copy16_to_lds_sv(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
       : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -234,14 +245,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   const int qh = g * kHpg + qs % kHpg;
   const bool qvalid = qs < kTileTokens * kHpg && qt <= t_last;
   const int nkv_q = qvalid ? a.pos0 + qt + 1 : 1;
-  half8_t qf[8];  // Q^T k-step s: dims 32 s + 8 j .. +7
-  {
-    const _Float16* qrow = a.q + ((int64_t)(qvalid ? qt : t0) * H + (qvalid ? qh : g * kHpg)) *
-                                     kHeadDim + 8 * j;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const half8_t*>(qrow + 32 * s);
-  }
-
   // ---- LDS read addresses of this lane's operand fragments
   // K: row (cell) 16 mt + n, group 4 s + j; s = 4 v + u -> the XOR touches
   // the low 4 bits only, so v and mt are immediates
@@ -253,16 +256,33 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) voff[kk] = lds_addr(kv) + 2 * kHalf + vimg_off(n, 4 * kk + j);
 
+  // wave w copies bytes [4096 w, 4096 w + 4096) of an image: lane i's 16
+  // bytes of each 1 KB piece at 16 i
+  uint32_t copy_voff[kCopyOps];
+#pragma unroll
+  for (int i = 0; i < kCopyOps; ++i) copy_voff[i] = w * (kHalf / kWaves) + 1024 * i + 16 * lane;
   auto issue_copy = [&](const uint8_t* src, uint32_t dst) {
-    const uint8_t* s = src + w * (kHalf / kWaves) + 16 * lane;
     const uint32_t d = dst + w * (kHalf / kWaves);
 #pragma unroll
-    for (int i = 0; i < kCopyOps; ++i) copy16_to_lds(s + 1024 * i, d + 1024 * i);
+    for (int i = 0; i < kCopyOps; ++i) copy16_to_lds_sv(src, copy_voff[i], d + 1024 * i);
   };
   auto copy_k = [&](int c) { issue_copy(img_g + (int64_t)c * kImg, lds_addr(kv) + (c & 1) * kHalf); };
   auto copy_v = [&](int c) {
     issue_copy(img_g + (int64_t)c * kImg + kHalf, lds_addr(kv) + (2 + (c & 1)) * kHalf);
   };
+
+  // the first chunk images stream in while Q loads
+  copy_k(0);
+  copy_v(0);
+  if (nch > 1) copy_k(1);
+
+  half8_t qf[8];  // Q^T k-step s: dims 32 s + 8 j .. +7
+  {
+    const _Float16* qrow = a.q + ((int64_t)(qvalid ? qt : t0) * H + (qvalid ? qh : g * kHpg)) *
+                                     kHeadDim + 8 * j;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const half8_t*>(qrow + 32 * s);
+  }
 
   auto lds16 = [](uint32_t addr) -> half8_t { return *(const lds_half8_t*)(uintptr_t)addr; };
 
@@ -338,7 +358,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
 
   // One pass over the block's chunks; returns true when the fast pass must
   // be redone exactly (SAFE = false only).
-  auto run = [&](auto SAFE_T) -> bool {
+  auto run = [&](auto SAFE_T, bool prefetched) -> bool {
     constexpr bool SAFE = decltype(SAFE_T)::value;
     f32x4 oacc[16];
 #pragma unroll
@@ -346,9 +366,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     float m_ref = -INFINITY, l_run = 0.f;
     bool over = false;
 
-    copy_k(0);
-    copy_v(0);
-    if (nch > 1) copy_k(1);
+    if (!prefetched) {
+      copy_k(0);
+      copy_v(0);
+      if (nch > 1) copy_k(1);
+    }
     wait_vmcnt0();
     wg_barrier();
     f32x4 s_cur[4];
@@ -366,18 +388,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       if constexpr (NEXT) scores(std::integral_constant<int, 1 - P>{}, s_nxt);
       mask(c, s_cur);
       const float cm = chunk_max(s_cur);
-      if constexpr (SAFE) {
-        const float m_new = fmaxf(m_ref, cm);
-        if (__builtin_amdgcn_ballot_w64(m_new > m_ref) != 0ull) {
-          const float alpha = fast_exp2(m_ref - m_new);  // 0 while m_ref = -inf
-          l_run *= alpha;
+      // exact online softmax (this step serves the exact pass only)
+      const float m_new = fmaxf(m_ref, cm);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_ref) != 0ull) {
+        const float alpha = fast_exp2(m_ref - m_new);  // 0 while m_ref = -inf
+        l_run *= alpha;
 #pragma unroll
-          for (int mt = 0; mt < 16; ++mt) oacc[mt] *= alpha;
-          m_ref = m_new;
-        }
-      } else {
-        m_ref = c == 0 ? cm : m_ref;  // chunk 0 always holds cell 0: finite
-        over |= qvalid && cm > m_ref + kMaxGrowth;
+        for (int mt = 0; mt < 16; ++mt) oacc[mt] *= alpha;
+        m_ref = m_new;
       }
       half8_t pb[2];
       probs(s_cur, m_ref, l_run, pb);
@@ -394,7 +412,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     // Every chunk runs the same body, so the buffer parity is a run-time
     // offset and the last chunk's score stages multiply a stale K image (in
     // bounds, untouched by copies) whose result is dropped.
-    auto step_fast = [&](int c) {
+    auto step_fast = [&](int c, f32x4 (&s_cur)[4], f32x4 (&s_nxt)[4]) {
       constexpr int kS = 8;            // score stages (k-steps of chunk c + 1)
       constexpr int kStages = kS + 8;  // then PV stages: k-step t / 4, m-tiles 4 (t % 4) ..
       constexpr int kAhead = 1;        // stages whose fragments are read ahead
@@ -404,27 +422,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       if (c + 2 < nch) copy_k(c + 2);
       if (c + 1 < nch) copy_v(c + 1);
       mask(c, s_cur);
+      // the chunk's buffer bases; every fragment is then base + immediate
+      uint32_t kb[4], vb[2];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) kb[x] = koff[x] + kpar;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) vb[kk] = voff[kk] + vpar;
       half8_t fr[kAhead + 1][4];
       auto load = [&](auto I, half8_t (&dst)[4]) {
         constexpr int i = decltype(I)::value;
         if constexpr (i < kS) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-            dst[mt] = lds16(koff[i & 3] + kpar + (256 * (i >> 2) + mt * 16 * (kHeadDim * 2)));
+            dst[mt] = lds16(kb[i & 3] + (256 * (i >> 2) + mt * 16 * (kHeadDim * 2)));
         } else {
           constexpr int t = i - kS;
 #pragma unroll
           for (int m = 0; m < 4; ++m)
-            dst[m] = lds16(voff[t >> 2] + vpar + ((4 * (t & 3) + m) * 16 * (kChunk * 2)));
+            dst[m] = lds16(vb[t >> 2] + ((4 * (t & 3) + m) * 16 * (kChunk * 2)));
         }
       };
-      f32x4 s_nxt[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) s_nxt[mt] = zero4();
       static_for<kAhead>([&](auto I) { load(I, fr[decltype(I)::value]); });
-      const float cm = chunk_max(s_cur);
-      m_ref = c == 0 ? cm : m_ref;  // chunk 0 always holds cell 0: finite
-      over |= qvalid && cm > m_ref + kMaxGrowth;
+      // chunk 0 always holds cell 0: the reference is finite
+      if (c == 0) m_ref = chunk_max(s_cur);
       const float nm = -m_ref;
       half8_t pb[2];  // P in B-operand slot order: k-step kk, slot e
       // exponentials of slots 2 i and 2 i + 1 (slot q = 8 kk + e), rounded
@@ -458,8 +480,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) s_cur[mt] = s_nxt[mt];
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
@@ -478,19 +498,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
         step(c, F_{}, P0{});
       }
     } else {
-      for (int c = 0; c < nch; ++c) step_fast(c);
+      // two chunks per trip: the score registers trade roles, no copies
+      f32x4 s_alt[4];
+      int c = 0;
+      for (; c + 1 < nch; c += 2) {
+        step_fast(c, s_cur, s_alt);
+        step_fast(c + 1, s_alt, s_cur);
+      }
+      if (c < nch) step_fast(c, s_cur, s_alt);
     }
 
+    // ---- finalise: O / l -> fp16; lane (n, j) holds dims 16 mt + 4 j + i
+    const float l_tot = lane_group_sum(l_run);
     if constexpr (!SAFE) {
-      // workgroup vote: a score beyond the reference by more than
-      // 2^kMaxGrowth anywhere in the block sends it to the exact pass
+      // workgroup vote: every P value is below l, so l < 65504 means no P
+      // overflowed fp16; otherwise (scores far above the chunk-0 reference)
+      // the block is redone exactly
+      over = qvalid && !(l_tot < kP16Max);
       if (__builtin_amdgcn_ballot_w64(over) != 0ull) s_redo = 1;
       __syncthreads();
       if (s_redo) return true;
     }
 
-    // ---- finalise: O / l -> fp16; lane (n, j) holds dims 16 mt + 4 j + i
-    const float l_tot = lane_group_sum(l_run);
     if (qvalid) {
       const float inv = 1.f / l_tot;
       _Float16* orow = a.out + ((int64_t)qt * H + qh) * kHeadDim + 4 * j;
@@ -511,7 +540,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   if (tid == 0) s_redo = 0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (run(std::false_type{})) run(std::true_type{});
+  if (run(std::false_type{}, true)) run(std::true_type{}, false);
 }
 
 int64_t tile_workspace_bytes(int G, int t_count, int pos0) {
