@@ -9,7 +9,8 @@ never imports it; the two meet only in the seeded input generator
 Two independent formulations live here:
   * ``qsa_oracle.c`` (built with gcc, OpenMP over (token, group) rows): the
     plain definition -- selection, then exact softmax attention over the
-    selected cells -- plus the chunk-partial and log-sum-exp merge steps;
+    selected cells -- plus the chunk-partial and log-sum-exp merge steps,
+    and the K/V quantiser that fills the int8 cache (decided in IEEE fp32);
   * ``dense_reference`` below: a numpy brute force over the full (token x
     cell) matrix with explicit causal and top-k masks, for tiny inputs.
 
@@ -61,8 +62,10 @@ def _load():
     lib.qsa_oracle_partials.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32,
                                         P, P, P, P, P, P, P, P, P]
     lib.qsa_oracle_merge.argtypes = [i32, i32, i32, i32, P, P, P]
+    lib.qsa_oracle_quantize.argtypes = [i64, i32, i32, P, P, P]
+    lib.qsa_oracle_f32_to_f16.argtypes = [i64, P, P]
     for f in (lib.qsa_oracle_select, lib.qsa_oracle_attend, lib.qsa_oracle_partials,
-              lib.qsa_oracle_merge):
+              lib.qsa_oracle_merge, lib.qsa_oracle_quantize, lib.qsa_oracle_f32_to_f16):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -207,6 +210,33 @@ def dense_reference(inp, scores: Optional[np.ndarray] = None) -> tuple:
         w /= w.sum(axis=1, keepdims=True)
         out[:, h, :] = w @ v[g]
     return out, mask
+
+
+def f32_to_f16(a: np.ndarray) -> np.ndarray:
+    """The oracle's own fp32 -> fp16 rounding (to nearest, ties to even)."""
+    lib = _load()
+    x = _c(a, np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    if lib.qsa_oracle_f32_to_f16(x.size, _ptr(x), _ptr(out)) != 0:
+        raise RuntimeError("qsa_oracle_f32_to_f16 failed")
+    return out.view(np.float16)
+
+
+def quantize(x: np.ndarray, block: int = 64) -> tuple:
+    """K/V quantiser: fp16 rows [..., D] -> (int8 codes [..., D], fp16
+    scales [..., D / block]); per block scale = fp16(absmax / 127) and
+    code = clamp(rint(x / scale), -127, 127), decided in IEEE fp32."""
+    lib = _load()
+    xh = np.ascontiguousarray(x, dtype=np.float16)
+    D = xh.shape[-1]
+    rows = xh.size // D if D else 0
+    codes = np.empty(xh.shape, dtype=np.int8)
+    scales = np.empty(xh.shape[:-1] + (D // block,), dtype=np.uint16)
+    rc = lib.qsa_oracle_quantize(rows, D, block, _ptr(xh.view(np.uint16)), _ptr(codes),
+                                 _ptr(scales))
+    if rc != 0:
+        raise RuntimeError("qsa_oracle_quantize failed")
+    return codes, scales.view(np.float16)
 
 
 def rel_l2(a: np.ndarray, b: np.ndarray) -> float:

@@ -262,3 +262,100 @@ int qsa_oracle_merge(int T, int H, int D, int KC, const int32_t *nchunks, const 
   }
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * K/V quantiser: the step that fills the int8 cache the path reads (the
+ * quantiser part of the pages' prep step; "sol_r6_qsa", delivered change:
+ * int8 codes with one fp16 scale per 64 dims).  The pages do not state the
+ * rounding rule; the reading taken is the plain absmax one, per row and
+ * 64-dim block b:
+ *   amax  = max_d |x[d]|                        (exact)
+ *   scale = fp16_rne(amax / 127)                (fp32 division, correctly rounded)
+ *   code  = clamp(rint(x[d] / scale), -127, 127)  (fp32 division, ties to even)
+ * and code = 0 for every d of a block whose scale is 0.  The decisions are
+ * taken in IEEE fp32 (the precision the GPU kernel uses), so codes and scales
+ * must match bit for bit.  Inputs are fp16 bit patterns and must be finite.
+ */
+
+/* fp16 bits -> float (exact). */
+static float f16_bits_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31;
+  const int exp = (h >> 10) & 31;
+  const uint32_t man = h & 1023u;
+  float v;
+  if (exp == 0) {
+    v = ldexpf((float)man, -24);                 /* zero or subnormal */
+  } else if (exp == 31) {
+    v = man ? NAN : INFINITY;
+  } else {
+    v = ldexpf((float)(man | 1024u), exp - 25);  /* 1.man * 2^(exp-15) */
+  }
+  uint32_t bits;
+  memcpy(&bits, &v, 4);
+  bits |= sign;
+  memcpy(&v, &bits, 4);
+  return v;
+}
+
+/* float -> fp16 bits, round to nearest, ties to even (IEEE 754 binary16). */
+static uint16_t f32_to_f16_bits_rne(float f) {
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  const uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+  const float a = fabsf(f);
+  if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+  if (a >= 65520.0f) return (uint16_t)(sign | 0x7c00u);   /* rounds past the largest finite */
+  if (a < ldexpf(1.0f, -14)) {
+    /* subnormal range: value = m * 2^-24, m = rint(a * 2^24) (exact scaling) */
+    const float m = rintf(ldexpf(a, 24));
+    return (uint16_t)(sign | (uint16_t)m);             /* m == 1024 gives the smallest normal */
+  }
+  int e;
+  const float fr = frexpf(a, &e);                      /* a = fr * 2^e, fr in [0.5, 1) */
+  const float m = rintf(ldexpf(fr, 11));               /* 11 significant bits, in [1024, 2048] */
+  uint32_t man = (uint32_t)m;
+  int exp = e - 1 + 15;                                /* biased exponent of 1.xxx * 2^(e-1) */
+  if (man == 2048u) {                                  /* rounded up to the next binade */
+    man = 1024u;
+    exp += 1;
+  }
+  if (exp >= 31) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | (uint16_t)(exp << 10) | (uint16_t)(man & 1023u));
+}
+
+int qsa_oracle_f32_to_f16(int64_t n, const float *in, uint16_t *out) {
+  if (n < 0 || (n && (!in || !out))) return ORACLE_BAD;
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16_bits_rne(in[i]);
+  return ORACLE_OK;
+}
+
+int qsa_oracle_quantize(int64_t rows, int D, int block, const uint16_t *x, int8_t *codes,
+                        uint16_t *scales) {
+  if (rows < 0 || D <= 0 || block <= 0 || D % block != 0) return ORACLE_BAD;
+  if (rows && (!x || !codes || !scales)) return ORACLE_BAD;
+  const int nb = D / block;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int b = 0; b < nb; ++b) {
+      const uint16_t *xb = x + r * D + (int64_t)b * block;
+      int8_t *cb = codes + r * D + (int64_t)b * block;
+      float amax = 0.0f;
+      for (int d = 0; d < block; ++d) {
+        const float v = fabsf(f16_bits_to_f32(xb[d]));
+        if (v > amax) amax = v;
+      }
+      const uint16_t sbits = f32_to_f16_bits_rne(amax / 127.0f);
+      scales[r * nb + b] = sbits;
+      const float s = f16_bits_to_f32(sbits);
+      for (int d = 0; d < block; ++d) {
+        float c = 0.0f;
+        if (s > 0.0f) {
+          c = rintf(f16_bits_to_f32(xb[d]) / s);
+          if (c > 127.0f) c = 127.0f;
+          if (c < -127.0f) c = -127.0f;
+        }
+        cb[d] = (int8_t)c;
+      }
+    }
+  }
+  return ORACLE_OK;
+}
