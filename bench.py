@@ -19,7 +19,12 @@ Other workloads (--workload):
                                   qsa_topk (top 2051 of up to 31,984
                                   cells) + qsa_flash with explicit ids;
   decode4_pos8192                 4 tokens at position 8192: qsa_topk,
-                                  split qsa_flash, qsa_merge.
+                                  split qsa_flash, qsa_merge;
+  quantize_kv_31984               the K/V quantiser on the long-context
+                                  cache: qsa_quantize of the fp16 K and V
+                                  rows of 2 groups x 31,984 cells per step
+                                  (cells quantised per second; roofline HBM
+                                  on 512 B in + 264 B out per row).
 
 One JSON line goes to stdout; progress goes to stderr.  A prompt step
 enqueues each layer's fused qsa_flash as its two halves, qsa_flash_prepare
@@ -66,7 +71,9 @@ WORKLOADS = {
     "t512_pos0_x12": dict(T=512, pos0=0, layers=12, kind="prompt"),
     "t1984_pos30000": dict(T=1984, pos0=30000, layers=1, kind="prompt"),
     "decode4_pos8192": dict(T=4, pos0=8192, layers=1, kind="decode"),
+    "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
 }
+QUANT_ROW_BYTES = 256 * 2 + 256 + 4 * 2  # fp16 row in; int8 codes + 4 fp16 scales out
 KERNEL_SOURCES = ("qsa_flash_tile.hip", "qsa_flash_rows.hip", "qsa_device.h")
 
 
@@ -173,6 +180,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("bench: calibration copy of %d MiB done" % args.calib_copy_mb)
+    if kind == "quantize":
+        bench_quantize(args, pos0 + T, dev)
+        return
 
     log("bench: generating %d layer(s) of inputs (%s)" % (L, args.workload))
     layers = []
@@ -293,6 +303,87 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle (bounded sample)")
         line["cpu_baseline"] = cpu_baseline(T, pos0, L)
+    print(json.dumps(line), flush=True)
+
+
+def bench_quantize(args, n_cells: int, dev) -> None:
+    """qsa_quantize on the fp16 K and V rows of a 2-group cache of n_cells
+    cells; one step quantises both tensors (two calls)."""
+    import numpy as np
+    import torch
+
+    import qsa_synth
+    import quantized_sparse_flash_amd as qsa
+
+    G = 2
+    rows = G * n_cells
+    log("bench: generating fp16 K/V rows (%d cells x %d groups)" % (n_cells, G))
+    xs = [torch.from_numpy(qsa_synth.kv_rows(rows, seed=s).reshape(G, n_cells, 256)).to(dev)
+          for s in (1, 2)]
+    codes = [torch.empty((G, n_cells, 256), dtype=torch.int8, device=dev) for _ in xs]
+    scales = [torch.empty((G, n_cells, 4), dtype=torch.float16, device=dev) for _ in xs]
+
+    def step(events=None):
+        for i in range(2):
+            if events is not None:
+                events[i][0].record()
+            qsa.qsa_quantize(xs[i], codes[i], scales[i])
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mean_launch_s = float(np.mean([e[0].elapsed_time(e[1]) for row in ev for e in row])) / 1e3
+    by = rows * QUANT_ROW_BYTES
+    gbs = by / mean_launch_s / 1e9
+    value = rows * args.steps / elapsed
+    log("bench: %.3f ms/step, quantize kernel mean %.1f us, %.0f GB/s"
+        % (elapsed / args.steps * 1e3, mean_launch_s * 1e6, gbs))
+    line = {
+        "metric": "qsa_quantize cells/s (K and V rows of 2 groups)",
+        "value": value,
+        "unit": "cells/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 in, int8 codes + fp16 scales out, fp32 decisions",
+        "data": "synthetic (seeded: fp16 N(0,1) x 10^U(-3,1) per 64-dim block)",
+        "config": {"workload": "%s: qsa_quantize of K and V, 2 groups x %d cells x 256 dims"
+                               % (args.workload, n_cells),
+                   "n_cells": n_cells, "n_groups": G, "head_dim": 256},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
+                     "kernel": "quantize_kernel (qsa_quantize)",
+                     "algorithmic_bytes_per_launch": by, "mean_launch_us": mean_launch_s * 1e6},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("bench: timing the CPU oracle quantiser (bounded sample)")
+        x0 = xs[0].cpu().numpy()
+        done, t_total = 0, 0.0
+        while t_total < 10.0 and done < 40:
+            t1 = time.perf_counter()
+            oracle.quantize(x0)
+            t_total += time.perf_counter() - t1
+            done += 1
+        # a cell is one K row and one V row: K-only passes count half a cell per row
+        line["cpu_baseline"] = {"value": done * rows / (2.0 * t_total), "unit": "cells/s",
+                                "cores": 1, "kind": "oracle",
+                                "sample": "%d passes of the oracle quantiser over the K rows "
+                                          "(%d rows, single thread), %.1f s; scaled to K+V "
+                                          "cells" % (done, rows, t_total)}
     print(json.dumps(line), flush=True)
 
 

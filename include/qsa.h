@@ -168,6 +168,29 @@ int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
  */
 int qsa_merge(const qsa_shape *shape, const float *part, _Float16 *out, void *stream);
 
+/*
+ * qsa_quantize -- the K/V quantiser that fills the int8 cache (the prep step
+ * of page "round 27 track b - qsa prep and merge"; the code/scale format of
+ * page "round 6 track b - qsa flash", delivered change: int8 codes, one fp16
+ * scale per 64 dims).  The pages give no rounding rule; this library's
+ * reading, per row and 64-dim block b:
+ *   scale[b] = fp16(absmax_b / 127),
+ *   code[d]  = clamp(rint(x[d] / scale[b]), -127, 127)   (0 if scale[b] == 0),
+ * both divisions correctly rounded IEEE fp32, rint and the fp16 conversion
+ * to nearest even: codes and scales are a deterministic function of x.
+ *   n_rows : rows to quantise (cells; call once for K and once for V, or
+ *            once over [G][n_cells] rows); 0 is a no-op.
+ *   dim    : dims per row; only 256 (QSA_HEAD_DIM) is supported.
+ *   x      : device, fp16 [n_rows][256], finite values.
+ *   codes  : device, int8 [n_rows][256]  (the kq / vq layout of qsa_flash).
+ *   scales : device, fp16 [n_rows][4]    (the ksc / vsc layout).
+ * Alignment: 16 bytes for x and codes, 2 bytes for scales.  Errors:
+ * QSA_ERR_UNSUPPORTED (dim), QSA_ERR_SHAPE (n_rows < 0 or too large),
+ * QSA_ERR_ARG (NULL or misaligned pointer).
+ */
+int qsa_quantize(int64_t n_rows, int32_t dim, const _Float16 *x, int8_t *codes,
+                 _Float16 *scales, void *stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *qsa_status_string(int status);
 

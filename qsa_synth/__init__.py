@@ -122,6 +122,41 @@ def score_rows(T: int, n_groups: int, n_cells: int, seed: int, *, kind: str = "n
     raise ValueError(kind)
 
 
+def kv_rows(n_rows: int, seed: int = SEED, *, kind: str = "mixed") -> np.ndarray:
+    """Unquantised fp16 K/V rows [n_rows][256] for quantiser tests and the
+    quantiser workload.
+
+    kind:
+      "mixed"  N(0,1) times a per-(row, 64-dim block) magnitude 10^U(-3, 1),
+               so blocks span tiny to large values (pre-quantisation K/V);
+      "edge"   blocks that are all zero, a single +-fp16 subnormal, the
+               fp16 extremes (+-65504), exact halves of the scale, or mixed.
+    """
+    rng = np.random.default_rng([seed, n_rows, 29])
+    if kind == "mixed":
+        mag = np.power(10.0, rng.uniform(-3.0, 1.0, (n_rows, HEAD_DIM // SCALE_BLOCK, 1)))
+        x = rng.standard_normal((n_rows, HEAD_DIM // SCALE_BLOCK, SCALE_BLOCK)) * mag
+        return x.reshape(n_rows, HEAD_DIM).astype(np.float16)
+    if kind == "edge":
+        nb = HEAD_DIM // SCALE_BLOCK
+        x = np.zeros((n_rows, nb, SCALE_BLOCK))
+        pick = rng.integers(0, 5, (n_rows, nb))
+        for r in range(n_rows):
+            for b in range(nb):
+                p = pick[r, b]
+                if p == 1:
+                    x[r, b, rng.integers(SCALE_BLOCK)] = rng.choice([-1, 1]) * 2.0 ** -24
+                elif p == 2:
+                    x[r, b] = rng.choice([-65504.0, 65504.0, 1.0, -3.0], SCALE_BLOCK)
+                elif p == 3:
+                    x[r, b] = rng.integers(-126, 126, SCALE_BLOCK) + 0.5
+                    x[r, b, 0] = 127.0
+                elif p == 4:
+                    x[r, b] = rng.standard_normal(SCALE_BLOCK) * 10.0 ** rng.uniform(-8, 4)
+        return np.clip(x, -65504.0, 65504.0).reshape(n_rows, HEAD_DIM).astype(np.float16)
+    raise ValueError(kind)
+
+
 # Named workloads (sizes of the pages' measured configurations).
 WORKLOADS = {
     # tiny prompt under budget: token t sees cells 0..t; one layer

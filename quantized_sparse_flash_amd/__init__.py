@@ -13,6 +13,7 @@ Entry points (all asynchronous on the current stream):
   qsa_flash_prepare(shape, kq, ksc, vq, vsc, workspace)         fused mode, first half
   qsa_flash_attend(shape, q, kq, ksc, vq, vsc, ids, out, workspace)   ... second half
   qsa_merge(shape, part, out)                                  LSE merge
+  qsa_quantize(x, codes, scales)                               K/V quantiser
 """
 from __future__ import annotations
 
@@ -37,7 +38,7 @@ DEFAULT_BUDGET = 2051
 MAX_BUDGET = 65536
 
 EXPORTED = ("qsa_topk", "qsa_flash", "qsa_flash_prepare", "qsa_flash_attend", "qsa_merge",
-            "qsa_status_string", "qsa_part_elems", "qsa_flash_workspace_bytes")
+            "qsa_quantize", "qsa_status_string", "qsa_part_elems", "qsa_flash_workspace_bytes")
 
 
 class QsaError(RuntimeError):
@@ -103,12 +104,13 @@ def load_library(path: str = LIB_PATH):
     lib.qsa_flash_workspace_bytes.argtypes = [SP]
     lib.qsa_flash_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_merge.argtypes = [SP, P, P, P]
+    lib.qsa_quantize.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, P, P]
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
     lib.qsa_part_elems.argtypes = [SP]
     lib.qsa_part_elems.restype = ctypes.c_int64
     for f in (lib.qsa_topk, lib.qsa_flash, lib.qsa_flash_prepare, lib.qsa_flash_attend,
-              lib.qsa_merge):
+              lib.qsa_merge, lib.qsa_quantize):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -269,3 +271,19 @@ def qsa_merge(shape: QsaShape, part, out, stream=None) -> None:
     rc = load_library().qsa_merge(ctypes.byref(cs), pp, op, _stream(stream))
     if rc != QSA_OK:
         raise QsaError(rc, "qsa_merge")
+
+
+def qsa_quantize(x, codes, scales, stream=None) -> None:
+    """Quantise fp16 rows [..., 256] into int8 ``codes`` (same shape) and fp16
+    ``scales`` [..., 4]: scale = fp16(absmax / 127) per 64-dim block, code =
+    clamp(rint(x / scale), -127, 127)."""
+    import torch
+    if x.dim() < 1 or x.shape[-1] != HEAD_DIM:
+        raise ValueError("x must have a last dimension of %d" % HEAD_DIM)
+    rows = x.numel() // HEAD_DIM
+    xp = _dev_ptr(x, "x", torch.float16)
+    cp = _dev_ptr(codes, "codes", torch.int8, tuple(x.shape))
+    sp = _dev_ptr(scales, "scales", torch.float16, tuple(x.shape[:-1]) + (HEAD_DIM // 64,))
+    rc = load_library().qsa_quantize(rows, HEAD_DIM, xp, cp, sp, _stream(stream))
+    if rc != QSA_OK:
+        raise QsaError(rc, "qsa_quantize")

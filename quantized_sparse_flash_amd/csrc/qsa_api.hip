@@ -184,4 +184,15 @@ int qsa_merge(const qsa_shape* s, const float* part, _Float16* out, void* stream
                                          s->pos0, s->budget, (hipStream_t)stream));
 }
 
+int qsa_quantize(int64_t n_rows, int32_t dim, const _Float16* x, int8_t* codes,
+                 _Float16* scales, void* stream) {
+  if (dim != QSA_HEAD_DIM) return QSA_ERR_UNSUPPORTED;
+  // one workgroup per 16 rows on a 1-D grid
+  if (n_rows < 0 || n_rows > (int64_t)INT32_MAX * 16) return QSA_ERR_SHAPE;
+  if (n_rows == 0) return QSA_OK;
+  if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2))
+    return QSA_ERR_ARG;
+  return launch_status(qsa::launch_quantize(x, codes, scales, n_rows, (hipStream_t)stream));
+}
+
 }  // extern "C"

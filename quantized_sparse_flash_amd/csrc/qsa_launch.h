@@ -24,6 +24,10 @@ hipError_t launch_topk(const float* scores, int32_t* ids, int T, int pos0, int G
                        int64_t n_cells, hipStream_t stream);
 hipError_t launch_merge(const float* part, _Float16* out, int T, int H, int pos0, int budget,
                         hipStream_t stream);
+// K/V quantiser: `rows` fp16 rows of 256 dims -> int8 codes and 4 fp16
+// scales per row.
+hipError_t launch_quantize(const _Float16* x, int8_t* codes, _Float16* scales, int64_t rows,
+                           hipStream_t stream);
 // Row kernel: one wavefront per (token, group) row for tokens [t_begin, T)
 // (fused), or per (token, group, chunk) for all tokens (split mode).
 hipError_t launch_flash_rows(const RowArgs& a, bool split, int t_begin, hipStream_t stream);

@@ -143,3 +143,19 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert _raw(lib, "qsa_topk", under, 0, 0, None) == E                          # ids
     assert _raw(lib, "qsa_merge", under, A, A + 2, None) == E
     assert _raw(lib, "qsa_merge", under, 0, A, None) == E
+
+
+def test_quantize_arguments_are_validated():
+    lib = qsa.load_library()
+    A = 0x10000
+    q = lambda rows, dim, x, c, s: lib.qsa_quantize(rows, dim, ctypes.c_void_p(x) if x else None,
+                                                     ctypes.c_void_p(c) if c else None,
+                                                     ctypes.c_void_p(s) if s else None, None)
+    assert q(0, 256, 0, 0, 0) == qsa.QSA_OK                       # nothing to do
+    assert q(4, 128, A, A, A) == qsa.QSA_ERR_UNSUPPORTED
+    assert q(-1, 256, A, A, A) == qsa.QSA_ERR_SHAPE
+    assert q(4, 256, 0, A, A) == qsa.QSA_ERR_ARG                  # x
+    assert q(4, 256, A + 8, A, A) == qsa.QSA_ERR_ARG              # x 16 B
+    assert q(4, 256, A, A + 4, A) == qsa.QSA_ERR_ARG              # codes 16 B
+    assert q(4, 256, A, A, A + 1) == qsa.QSA_ERR_ARG              # scales 2 B
+    assert q(4, 256, A, A, 0) == qsa.QSA_ERR_ARG
