@@ -74,7 +74,7 @@ WORKLOADS = {
     "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
 }
 QUANT_ROW_BYTES = 256 * 2 + 256 + 4 * 2  # fp16 row in; int8 codes + 4 fp16 scales out
-KERNEL_SOURCES = ("qsa_flash_tile.hip", "qsa_flash_rows.hip", "qsa_device.h")
+KERNEL_SOURCES = ("qsa_flash_tile.hip", "qsa_flash_rows.hip", "qsa_quantize.hip", "qsa_device.h")
 
 
 def log(*a):
