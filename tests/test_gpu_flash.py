@@ -206,3 +206,20 @@ def test_prepare_then_attend_equals_fused_call(T, pos0):
     got = out.cpu().numpy().astype(np.float64)
     np.testing.assert_array_equal(got, fused)
     _check(got, oracle.attend(inp, ids))
+
+
+def test_maximum_budget():
+    # budget at the library's limit (65,536 cells): selection runs the
+    # streaming top-k (rows longer than 32,768 cells), each row walks 1,024
+    # chunks in the row kernel, and split mode writes 1,024 records per head
+    T, pos0, budget = 2, 70000, 65536
+    inp = qsa_synth.layer_inputs(T, pos0, seed=41, budget=budget)
+    ids = oracle.select(T, pos0, budget, inp.scores, 2, inp.n_cells)
+    dev = upload(inp)
+    np.testing.assert_array_equal(gpu_topk(inp, dev), ids)
+    ref = oracle.attend(inp, ids)
+    _check(gpu_flash(inp, ids, dev), ref)
+    from gpu_util import gpu_merge
+    part = gpu_flash(inp, ids, dev, split=True)
+    assert part.shape[1] == budget // 64
+    _check(gpu_merge(inp, part), ref)
