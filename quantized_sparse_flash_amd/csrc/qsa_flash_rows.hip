@@ -121,6 +121,27 @@ void flash_rows_kernel(RowArgs a) {
     const int my_cell = clamp_cell(next_raw);
     next_raw = raw_id(k + 1);
 
+    // V codes and scales of k-step kk: lane (n, j) takes dims 16n..16n+15
+    // of the cells at positions 4j + i and 16 + 4j + i of the 32-cell half
+    auto load_v = [&](int kk, u32x4 (&vrow)[8], uint32_t (&vs)[8]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pos = 32 * kk + ((i < 4) ? (4 * j + i) : (16 + 4 * j + (i - 4)));
+        const int cell = __shfl(my_cell, pos);
+        vrow[i] = *reinterpret_cast<const u32x4*>(vq_g + (int64_t)cell * kHeadDim + 16 * n);
+        vs[i] = *reinterpret_cast<const uint16_t*>(vsc_g + (int64_t)cell * kNBlk + (n >> 2));
+      }
+    };
+    // split mode handles one chunk per wave: its V loads go out with K's
+    // (one memory round trip instead of two); the fused loop keeps V's
+    // registers free until the scores are done
+    u32x4 vrow_s[2][8];
+    uint32_t vs_s[2][8];
+    if constexpr (SPLIT) {
+      load_v(0, vrow_s[0], vs_s[0]);
+      load_v(1, vrow_s[1], vs_s[1]);
+    }
+
     // ---- S^T = K Q^T, four 16-cell m-tiles
     f32x4 sacc[4];
 #pragma unroll
@@ -201,12 +222,14 @@ void flash_rows_kernel(RowArgs a) {
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 vrow[8];
       uint32_t vs[8];
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int pos = 32 * kk + ((i < 4) ? (4 * j + i) : (16 + 4 * j + (i - 4)));
-        const int cell = __shfl(my_cell, pos);
-        vrow[i] = *reinterpret_cast<const u32x4*>(vq_g + (int64_t)cell * kHeadDim + 16 * n);
-        vs[i] = *reinterpret_cast<const uint16_t*>(vsc_g + (int64_t)cell * kNBlk + (n >> 2));
+        for (int i = 0; i < 8; ++i) {
+          vrow[i] = vrow_s[kk][i];
+          vs[i] = vs_s[kk][i];
+        }
+      } else {
+        load_v(kk, vrow, vs);
       }
       half2_t sp[4];
 #pragma unroll
