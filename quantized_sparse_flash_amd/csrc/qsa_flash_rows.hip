@@ -35,6 +35,7 @@
 namespace qsa {
 
 constexpr float kLazyGrowth = 8.0f;  // log2 headroom of the running reference max
+constexpr int kXcds = 8;             // XCDs that workgroups are dealt to, round robin
 
 
 __device__ __forceinline__ half2_t splat_lo(uint32_t u) {
@@ -53,16 +54,28 @@ template <bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_rows_kernel(RowArgs a) {
   const int lane = threadIdx.x & 63;
-  // wave-uniform: every per-row value below lives in scalar registers
-  const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (item >= a.n_items) return;
   const int G = a.G, H = G * kHpg;
   int t, g, k_only = 0;
   if (SPLIT) {
+    // wave-uniform: every per-row value below lives in scalar registers
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (item >= a.n_items) return;
     g = item % G;
     k_only = (item / G) % a.KC;
     t = item / (G * a.KC);
+  } else if (kXcds % G == 0) {
+    // workgroups are dealt to the XCDs round robin: XCD x serves group
+    // x % G only, so each XCD's L2 caches one group's cells
+    const int per = kXcds / G;
+    const int b = blockIdx.x, x = b % kXcds;
+    const int r = __builtin_amdgcn_readfirstlane(4 * ((b / kXcds) * per + x / G) +
+                                                 (threadIdx.x >> 6));
+    g = x % G;
+    if (r >= a.n_items / G) return;
+    t = a.T - 1 - r;  // longest rows first
   } else {
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (item >= a.n_items) return;
     g = item % G;
     t = a.T - 1 - item / G;  // longest rows first
   }
@@ -285,6 +298,12 @@ hipError_t launch_flash_rows(const RowArgs& args_in, bool split, int t_begin,
   a.n_items = split ? a.T * a.KC * a.G : (a.T - t_begin) * a.G;
   if (a.n_items <= 0) return hipSuccess;
   dim3 grid((a.n_items + 3) / 4), block(256);
+  if (!split && kXcds % a.G == 0) {
+    // kXcds / G workgroup slots per round serve each group, 4 rows apiece
+    const int per = kXcds / a.G;
+    const int wgs_per_group = (a.T - t_begin + 3) / 4;
+    grid = dim3(kXcds * ((wgs_per_group + per - 1) / per));
+  }
   if (split)
     flash_rows_kernel<true><<<grid, block, 0, stream>>>(a);
   else
