@@ -74,7 +74,12 @@ WORKLOADS = {
     "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
 }
 QUANT_ROW_BYTES = 256 * 2 + 256 + 4 * 2  # fp16 row in; int8 codes + 4 fp16 scales out
-KERNEL_SOURCES = ("qsa_flash_tile.hip", "qsa_flash_rows.hip", "qsa_quantize.hip", "qsa_device.h")
+# sources of the kernel whose HBM traffic each workload's record describes
+TRAFFIC_SOURCES = {
+    "t1984_pos0_x12": ("qsa_flash_tile.hip", "qsa_device.h"),
+    "t1984_pos30000": ("qsa_flash_rows.hip", "qsa_device.h"),
+    "quantize_kv_31984": ("qsa_quantize.hip", "qsa_device.h"),
+}
 
 
 def log(*a):
@@ -95,9 +100,9 @@ def algorithmic(T: int, pos0: int, budget: int, G: int = 2):
     return visits, by, visits * FLOPS_PER_VISIT
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(names) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "quantized_sparse_flash_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -114,7 +119,8 @@ def measured_traffic(workload: str):
         for line in f:
             if line.startswith("{"):
                 rec = json.loads(line)
-    if not rec or rec.get("kernel_sources_sha256") != kernel_source_hash():
+    names = TRAFFIC_SOURCES.get(workload)
+    if not rec or not names or rec.get("kernel_sources_sha256") != kernel_source_hash(names):
         return None
     return rec.get("hbm_bytes_per_launch")
 
