@@ -14,10 +14,13 @@
 // ascending index order.
 //
 //   topk_regs_kernel (rows of at most 512 x 64 cells): the row is read from
-//     HBM once, coalesced, into registers (EPT keys per thread).  Three
-//     radix passes of 11, 11 and 10 bits count digits with LDS atomics; only
-//     the first pass touches every key, the later ones only keys that match
-//     the prefix found so far.  The selection is then two LDS bitmaps over
+//     HBM once, coalesced, into registers (EPT keys per thread).  A sample
+//     of 1024 keys gives a threshold that leaves, as a rule, a few thousand
+//     keys at or above it; those are counted exactly and copied to an LDS
+//     list, and three radix passes of 11, 11 and 10 bits (LDS atomics) run
+//     over the list alone.  When the list would not hold budget..6144 keys,
+//     the passes run over the registers instead (every key in the first
+//     pass, then only keys that match the prefix found so far).  The selection is then two LDS bitmaps over
 //     the row's cells (key > K, key == K), built from one ballot per 64
 //     cells, and two block-wide scans over the bitmap words: the first keeps
 //     the first krem equal keys, the second gives every selected cell its
@@ -174,17 +177,84 @@ topk_regs_kernel(const float* __restrict__ scores,
     __syncthreads();
   };
 
-  // first digit: bits 31..21 of every key, counted as the loads land (each
-  // key is converted, then counted; fences every 8 keys keep the scheduler
-  // from computing all bin addresses at once)
+  // every key, converted (cells past the row's end get key 0)
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    key[i] = score_key(__builtin_bit_cast(float, key[i]));
+    if (NT * (i + 1) > n32)  // slice reaches past the row's end (a scalar test)
+      key[i] = tid < n32 - NT * i ? key[i] : 0u;
+  }
+
+  // ---- a threshold from a sample.  Every thread draws two keys from the
+  // row's live slots; the digit (bits 31..21) of the sample's r-th largest
+  // key, r set four standard deviations above the sample's expected count
+  // of selected cells, gives t = digit << 21, which usually leaves between
+  // budget and kListCap keys at or above it.  Those keys go to the list and
+  // the exact select runs on them alone (the budget-th largest key of the
+  // row is the budget-th largest of the list whenever the list holds at
+  // least budget keys).  Otherwise the full passes below run.
+  bool listed = false;
+  {
+    const int live_slots = (n32 + NT - 1) / NT;
+    uint32_t smp[2];
+#pragma unroll
+    for (int sm = 0; sm < 2; ++sm) {
+      const int target = (tid * 37 + sm * 13 + 7) % live_slots;
+      uint32_t v = 0u;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) v = (i == target) ? key[i] : v;
+      smp[sm] = v;
+    }
+    clear_hist(2048);
+    atomicAdd(&hist[0][smp[0] >> 21], 1u);
+    atomicAdd(&hist[0][smp[1] >> 21], 1u);
+    __syncthreads();
+    const float expect = (float)budget * (2.0f * NT) / (float)n32;
+    const uint32_t r = (uint32_t)fminf(expect + 4.0f * sqrtf(expect) + 1.0f, 2.0f * NT);
+    krem = r;
+    choose(21, false);
+    const uint32_t t = prefix;  // the sample digit, bits 20..0 zero
+    prefix = 0;
+    krem = (uint32_t)budget;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) mine += key[i] >= t ? 1u : 0u;
+    uint32_t n_at;
+    uint32_t pos = block_excl_sum<NT>(mine, wsum, n_at);
+    if (n_at >= (uint32_t)budget && n_at <= (uint32_t)kListCap) {
+      listed = true;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i)
+        if (key[i] >= t) list[pos++] = key[i];
+      clear_hist(2048);  // (its barrier also publishes the list)
+      for (int j = tid; j < (int)n_at; j += NT) atomicAdd(&hist[0][list[j] >> 21], 1u);
+      __syncthreads();
+      choose(21, false);
+      clear_hist(2048);
+      for (int j = tid; j < (int)n_at; j += NT) {
+        const uint32_t k = list[j];
+        if ((k >> 21) == (prefix >> 21)) atomicAdd(&hist[0][(k >> 10) & 0x7ffu], 1u);
+      }
+      __syncthreads();
+      choose(10, false);
+      clear_hist(2048);
+      for (int j = tid; j < (int)n_at; j += NT) {
+        const uint32_t k = list[j];
+        if ((k >> 10) == (prefix >> 10)) atomicAdd(&hist[0][k & 0x3ffu], 1u);
+      }
+      __syncthreads();
+      choose(0, false);
+    }
+  }
+
+  if (!listed) {
+  // first digit: bits 31..21 of every key (fences every 8 keys keep the
+  // scheduler from computing all bin addresses at once)
   clear_hist(4 * 2048);
   {
     uint32_t* h = hist[lane >> 4];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
-      key[i] = score_key(__builtin_bit_cast(float, key[i]));
-      if (NT * (i + 1) > n32)  // slice reaches past the row's end (a scalar test)
-        key[i] = tid < n32 - NT * i ? key[i] : 0u;
       atomicAdd(&h[key[i] >> 21], 1u);
       if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
@@ -193,7 +263,6 @@ topk_regs_kernel(const float* __restrict__ scores,
   choose(21, true);
   const uint32_t d1 = prefix >> 21;
   const uint32_t n1 = eq_count;  // keys whose first digit is d1 (they hold the answer)
-
   if (n1 <= (uint32_t)kListCap) {
     // survivors of the first digit -> list, wave by wave in cell order
     uint32_t cnt = 0;
@@ -239,6 +308,7 @@ topk_regs_kernel(const float* __restrict__ scores,
     __syncthreads();
     choose(0, false);
   }
+  }  // !listed
   const uint32_t K = prefix;  // krem (1 <= krem <= eq_count) cells with key K are taken
 
   // ---- bitmaps: element row i of wave w covers cells [NT i + 64 w, +64)

@@ -85,3 +85,19 @@ def test_topk_rows_at_register_tile_edges(T, pos0):
     inp = _inputs_with_scores(T, pos0, 2051, "quantized", seed=pos0)
     ref = oracle.select(T, pos0, 2051, inp.scores, 2, inp.n_cells)
     np.testing.assert_array_equal(gpu_topk(inp), ref)
+
+
+@pytest.mark.parametrize("kind", ["quantized", "signed_zero", "gap"])
+def test_topk_register_rows_with_ties_and_gaps(kind):
+    # rows of 20,000..20,003 cells: four score levels, or a gap between the
+    # selected scores and a dense rest, stay on the sampled-threshold list;
+    # mostly-zero rows put ~19,000 keys at or above the sampled threshold,
+    # more than the LDS list holds, so the full register passes run
+    T, pos0, B = 4, 20000, 2051
+    inp = _inputs_with_scores(T, pos0, B, "normal" if kind == "gap" else kind, seed=77)
+    if kind == "gap":
+        s = inp.scores
+        s[:, :, :B] += np.float32(100.0)  # the first budget cells stand far above the rest
+        inp.scores = s
+    ref = oracle.select(T, pos0, B, inp.scores, 2, inp.n_cells)
+    np.testing.assert_array_equal(gpu_topk(inp), ref)
