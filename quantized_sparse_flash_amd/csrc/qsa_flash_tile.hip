@@ -88,27 +88,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // 64 lanes x 16 bytes from global memory straight into LDS: lane i's 16
-// bytes at `g` land at LDS byte lds + 16 i (lds must be wave-uniform).
-// Written as inline asm so that the compiler does not track the LDS write:
-// it would otherwise make every later LDS read wait for the copy to
-// complete, which serialises the prefetch with the math.  Completion is
-// awaited explicitly (s_waitcnt vmcnt) before a barrier publishes the data.
-// The asm loads M0 itself; nothing else in this kernel uses M0 (DS
-// instructions on gfx9+ do not read it), so the clobber is harmless here.
+// bytes at base + voff (voff per lane, base wave-uniform) land at LDS byte
+// lds + 16 i (lds must be wave-uniform).  Written as inline asm so that the
+// compiler does not track the LDS write: it would otherwise make every later
+// LDS read wait for the copy to complete, which serialises the prefetch with
+// the math.  Completion is awaited explicitly (s_waitcnt vmcnt) before a
+// barrier publishes the data.  The asm loads M0 itself; nothing else in this
+// kernel uses M0 (DS instructions on gfx9+ do not read it), so the clobber is
+// harmless here.  No immediate offset is used: on this copy the offset field
+// moves the LDS destination as well as the global source.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-      : "memory", "m0");
-}
-// The same copy from the wave-uniform base `base` plus the per-lane byte
-// offset `voff` (no immediate offset): no per-copy address math.
-__device__ __forceinline__ void copy16_to_lds_sv(const void* base, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
@@ -264,7 +255,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   auto issue_copy = [&](const uint8_t* src, uint32_t dst) {
     const uint32_t d = dst + w * (kHalf / kWaves);
 #pragma unroll
-    for (int i = 0; i < kCopyOps; ++i) copy16_to_lds_sv(src, copy_voff[i], d + 1024 * i);
+    for (int i = 0; i < kCopyOps; ++i) copy16_to_lds(src, copy_voff[i], d + 1024 * i);
   };
   auto copy_k = [&](int c) { issue_copy(img_g + (int64_t)c * kImg, lds_addr(kv) + (c & 1) * kHalf); };
   auto copy_v = [&](int c) {
