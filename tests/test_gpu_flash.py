@@ -223,3 +223,21 @@ def test_maximum_budget():
     part = gpu_flash(inp, ids, dev, split=True)
     assert part.shape[1] == budget // 64
     _check(gpu_merge(inp, part), ref)
+
+
+@pytest.mark.parametrize("G", [1, 3, 4])
+@pytest.mark.parametrize("T,pos0", [(70, 0), (40, 2030), (6, 5000)])
+def test_other_group_counts(G, T, pos0):
+    # 12 heads per group, G groups: the tile kernel's group interleave, the
+    # row kernel's per-XCD group mapping (G dividing the 8 XCDs) and its
+    # plain mapping (G = 3), selection and split + merge
+    inp = qsa_synth.layer_inputs(T, pos0, seed=G * 100 + T, n_groups=G)
+    ids = None
+    dev = upload(inp)
+    if inp.scores is not None:
+        ids = oracle.select(T, pos0, inp.budget, inp.scores, G, inp.n_cells)
+        np.testing.assert_array_equal(gpu_topk(inp, dev), ids)
+    ref = oracle.attend(inp, ids)
+    _check(gpu_flash(inp, ids, dev), ref)
+    from gpu_util import gpu_merge
+    _check(gpu_merge(inp, gpu_flash(inp, ids, dev, split=True)), ref)
