@@ -285,7 +285,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (value / m5) if m5 else None,
-        "dtype": "int8 K/V codes, fp16 scales/Q/P/out, fp32 accumulate",
+        "dtype": "f16",
+        "precision": "int8 K/V codes with fp16 scales, dequantised to fp16; fp16 Q, P and out; "
+                     "fp16 MFMA with fp32 accumulation",
         "data": "synthetic (seeded: q N(0,1) fp16, codes U[-127,127], scales U[0.002,0.02]"
                 "%s)" % (", scores N(0,1) fp32" if pos0 + T > budget else ""),
         "config": {"workload": "%s: T=%d pos0=%d, %d layer(s) of %s%s, 2 KV groups x 12 "
@@ -364,7 +366,9 @@ def bench_quantize(args, n_cells: int, dev) -> None:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 in, int8 codes + fp16 scales out, fp32 decisions",
+        "dtype": "f32",
+        "precision": "fp16 rows in, int8 codes + fp16 scales out; divisions and rounding "
+                     "decisions in IEEE fp32",
         "data": "synthetic (seeded: fp16 N(0,1) x 10^U(-3,1) per 64-dim block)",
         "config": {"workload": "%s: qsa_quantize of K and V, 2 groups x %d cells x 256 dims"
                                % (args.workload, n_cells),
