@@ -28,9 +28,18 @@ Other workloads (--workload):
 
 One JSON line goes to stdout; progress goes to stderr.  A prompt step
 enqueues each layer's fused qsa_flash as its two halves, qsa_flash_prepare
-(the dequantisation prepass) and qsa_flash_attend; HIP events on the launch
-stream bracket every attend call (decode: every split qsa_flash call), the
-path's dominant kernel.  The line carries
+(the dequantisation prepass) and qsa_flash_attend.  Without --warmup the
+warmup runs for 0.3 s, long enough for the GPU clock to settle under load
+(with a few steps only it is still rising, and a short timed region reads
+10% slow); without --steps the timed region lasts about 0.2 s (at least 20
+steps).  Two timed regions of K steps follow: the first, with nothing
+between kernels, gives value and ms_per_step; in the second, HIP events on
+the launch stream bracket each step's dominant launches (the attend calls,
+run back to back after every layer is prepared into its own workspace;
+decode: the split qsa_flash call, repeated), for the roofline figures.  An
+event between two kernels costs the stream a few microseconds and would
+count the dispatch of the next kernel as part of it, which is why the
+regions are apart.  The line carries
   roofline      that kernel against the resource that binds it: for prompt
                 chunks whose tokens are all under budget the tile kernel
                 shares every dequantised chunk among 120 queries, so its
@@ -73,6 +82,43 @@ WORKLOADS = {
     "decode4_pos8192": dict(T=4, pos0=8192, layers=1, kind="decode"),
     "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
 }
+AUTO_WARMUP_S = 0.3  # default warmup: the GPU clock takes tens of ms under load to settle
+AUTO_TIMED_S = 0.2    # default timed region length
+MIN_STEPS = 20
+
+
+def run_warmup(args, step, sync):
+    """Runs the warmup steps: exactly args.warmup of them when given, else
+    steps until AUTO_WARMUP_S has passed (at least 3).  Fills in args.warmup
+    and, when not given, args.steps (enough steps for about AUTO_TIMED_S).
+    Returns nothing; the caller's timed regions follow."""
+    t0 = time.perf_counter()
+    n = 0
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        sync()
+        n = args.warmup
+    else:
+        while n < 3 or time.perf_counter() - t0 < AUTO_WARMUP_S:
+            step()
+            n += 1
+            if n % 8 == 0:
+                sync()
+        sync()
+        args.warmup = n
+    if args.steps is None:
+        per_step = (time.perf_counter() - t0) / max(n, 1)
+        args.steps = max(MIN_STEPS, min(5000, int(AUTO_TIMED_S / max(per_step, 1e-6))))
+
+
+DECODE_REPEAT = 16  # split qsa_flash launches per kernel-timing step (decode)
+QUANT_REPEAT = 8    # K and V qsa_quantize launch pairs per kernel-timing step
+LAUNCH_TIMING = ("HIP events on the launch stream around each step's dominant launches, run "
+                 "back to back (every layer prepared first; decode: the split flash call "
+                 "%d times; quantiser: the step %d times), over a second timed region of K "
+                 "steps; value and ms_per_step come from the first region, which has no "
+                 "events" % (DECODE_REPEAT, QUANT_REPEAT))
 QUANT_ROW_BYTES = 256 * 2 + 256 + 4 * 2  # fp16 row in; int8 codes + 4 fp16 scales out
 # sources of the kernel whose HBM traffic each workload's record describes
 TRAFFIC_SOURCES = {
@@ -154,8 +200,12 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: enough for about %.1f s, at least %d)"
+                         % (AUTO_TIMED_S, MIN_STEPS))
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: steps until %.2f s have passed, "
+                         "which lets the GPU clock settle)" % AUTO_WARMUP_S)
     ap.add_argument("--workload", default="t1984_pos0_x12", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -214,50 +264,83 @@ def main():
     torch.cuda.synchronize()
     budget = layers[0]["shape"].budget
 
-    def step(events=None):
-        for i, d in enumerate(layers):
+    def step():
+        for d in layers:
             s = d["shape"]
             if d["scores"] is not None:
                 qsa.qsa_topk(s, d["scores"], d["ids"])
-            if kind != "decode":
-                qsa.qsa_flash_prepare(s, d["kq"], d["ksc"], d["vq"], d["vsc"], workspace=ws)
-            if events is not None:
-                events[i][0].record()
             if kind == "decode":
                 qsa.qsa_flash(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"], None,
                               d["part"])
+                qsa.qsa_merge(s, d["part"], d["out"])
             else:
+                qsa.qsa_flash_prepare(s, d["kq"], d["ksc"], d["vq"], d["vsc"], workspace=ws)
                 qsa.qsa_flash_attend(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"],
                                      d["out"], workspace=ws)
-            if events is not None:
-                events[i][1].record()
-            if kind == "decode":
-                qsa.qsa_merge(s, d["part"], d["out"])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def step_timed(ev0, ev1) -> int:
+        """The same step with its dominant launches back to back between two
+        events: every layer is prepared (into its own workspace) before the
+        attend launches run; a decode step's split qsa_flash call, which
+        only rewrites its partials, runs DECODE_REPEAT times.  Returns the
+        number of launches between the events."""
+        if kind == "decode":
+            for d in layers:
+                qsa.qsa_topk(d["shape"], d["scores"], d["ids"])
+            ev0.record()
+            for _ in range(DECODE_REPEAT):
+                for d in layers:
+                    qsa.qsa_flash(d["shape"], d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"],
+                                  d["ids"], None, d["part"])
+            ev1.record()
+            for d in layers:
+                qsa.qsa_merge(d["shape"], d["part"], d["out"])
+            return DECODE_REPEAT * L
+        for d in layers:
+            s = d["shape"]
+            if d["scores"] is not None:
+                qsa.qsa_topk(s, d["scores"], d["ids"])
+            qsa.qsa_flash_prepare(s, d["kq"], d["ksc"], d["vq"], d["vsc"], workspace=d["ws"])
+        ev0.record()
+        for d in layers:
+            qsa.qsa_flash_attend(d["shape"], d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"],
+                                 d["ids"], d["out"], workspace=d["ws"])
+        ev1.record()
+        return L
 
-    # timed region: K steps; HIP events bracket each qsa_flash call on the
-    # stream it is launched on (torch's current stream)
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(L)] for _ in range(args.steps)]
+    run_warmup(args, step, torch.cuda.synchronize)
+
+    # timed region 1 (value, ms_per_step): K steps with nothing else on the
+    # stream.  An event between two kernels costs the stream a few
+    # microseconds and reads the next kernel's dispatch as part of its time,
+    # so the launch durations come from a second region.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(ev[k])
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    launch_ms = [e[0].elapsed_time(e[1]) for row in ev for e in row]
-    mean_launch_s = float(np.mean(launch_ms)) / 1e3
+    # timed region 2 (roofline): K more steps, HIP events on the launch
+    # stream (torch's current stream) around each step's dominant launches
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+          for _ in range(args.steps)]
+    n_launch = 0
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(args.steps):
+        n_launch += step_timed(*ev[k])
+    torch.cuda.synchronize()
+    elapsed_ev = time.perf_counter() - t1
+    mean_launch_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) / n_launch / 1e3
 
     ms_per_step = elapsed / args.steps * 1e3
     value = T * args.steps / elapsed
     visits, by, flops = algorithmic(T, pos0, budget)
     gbs = by / mean_launch_s / 1e9
     tflops = flops / mean_launch_s / 1e12
-    log("bench: %.3f ms/step, attention kernel mean %.1f us, %.0f GB/s algorithmic, "
-        "%.1f TFLOP/s" % (ms_per_step, mean_launch_s * 1e6, gbs, tflops))
+    log("bench: %.3f ms/step (%.3f in the kernel-timing region), attention kernel mean %.1f us, "
+        "%.0f GB/s algorithmic, %.1f TFLOP/s"
+        % (ms_per_step, elapsed_ev / args.steps * 1e3, mean_launch_s * 1e6, gbs, tflops))
 
     traffic = measured_traffic(args.workload)
     identity_tile = pos0 + T <= budget and kind == "prompt"
@@ -265,13 +348,15 @@ def main():
         roofline = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
                     "traffic": traffic, "kernel": "flash_tile_kernel (qsa_flash_attend)",
-                    "flops_per_launch": flops, "mean_launch_us": mean_launch_s * 1e6}
+                    "flops_per_launch": flops, "mean_launch_us": mean_launch_s * 1e6,
+                    "launch_timing": LAUNCH_TIMING}
     else:
         roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                     "kernel": ("flash_rows_kernel<true> (split qsa_flash)" if kind == "decode"
                                else "flash_rows_kernel<false> (qsa_flash_attend)"),
-                    "algorithmic_bytes_per_launch": by, "mean_launch_us": mean_launch_s * 1e6}
+                    "algorithmic_bytes_per_launch": by, "mean_launch_us": mean_launch_s * 1e6,
+                    "launch_timing": LAUNCH_TIMING}
     m5 = PAGES_M5_TOKS.get(T) if (pos0 == 0 and L == 12) else None
     steps_desc = {"prompt": "qsa_flash", "decode": "qsa_topk + split qsa_flash + qsa_merge"}
     line = {
@@ -331,25 +416,28 @@ def bench_quantize(args, n_cells: int, dev) -> None:
     codes = [torch.empty((G, n_cells, 256), dtype=torch.int8, device=dev) for _ in xs]
     scales = [torch.empty((G, n_cells, 4), dtype=torch.float16, device=dev) for _ in xs]
 
-    def step(events=None):
+    def step():
         for i in range(2):
-            if events is not None:
-                events[i][0].record()
             qsa.qsa_quantize(xs[i], codes[i], scales[i])
-            if events is not None:
-                events[i][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(2)] for _ in range(args.steps)]
+    run_warmup(args, step, torch.cuda.synchronize)
+    # value from K plain steps; launch durations from K more steps, each
+    # repeated QUANT_REPEAT times between two events
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(ev[k])
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    mean_launch_s = float(np.mean([e[0].elapsed_time(e[1]) for row in ev for e in row])) / 1e3
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+          for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record()
+        for _ in range(QUANT_REPEAT):
+            step()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    mean_launch_s = (sum(e0.elapsed_time(e1) for e0, e1 in ev)
+                     / (2 * QUANT_REPEAT * args.steps) / 1e3)
     by = rows * QUANT_ROW_BYTES
     gbs = by / mean_launch_s / 1e9
     value = rows * args.steps / elapsed
@@ -376,7 +464,8 @@ def bench_quantize(args, n_cells: int, dev) -> None:
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
                      "kernel": "quantize_kernel (qsa_quantize)",
-                     "algorithmic_bytes_per_launch": by, "mean_launch_us": mean_launch_s * 1e6},
+                     "algorithmic_bytes_per_launch": by, "mean_launch_us": mean_launch_s * 1e6,
+                     "launch_timing": LAUNCH_TIMING},
     }
     if not args.no_cpu_baseline:
         import oracle

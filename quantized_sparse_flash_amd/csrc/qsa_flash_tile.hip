@@ -13,7 +13,8 @@
 // and then runs a plain fp16 flash kernel over the result:
 //
 //   dequant_chunks_kernel  one workgroup per (group, 64-cell chunk, 32-cell
-//     half): int8 code x fp16 scale -> fp16 (the value is rounded to fp16
+//     half), one wave per V^T slot group of the half: int8 code x fp16
+//     scale -> fp16 (the value is rounded to fp16
 //     once, as when the pages' kernel fills its K/V tiles), written to the
 //     workspace as the two 32 KB images the attention kernel copies verbatim
 //     into LDS:
@@ -75,7 +76,7 @@ constexpr float kP16Max = 65504.0f;         // largest finite fp16
 constexpr int kHalf = kChunk * kHeadDim * 2;  // bytes of one K or V^T image (32 KB)
 constexpr int kImg = 2 * kHalf;               // bytes per (group, chunk) in the workspace
 constexpr int kCopyOps = kHalf / 1024 / kWaves;  // 1 KB copies per wave per image (4)
-constexpr int kHalfCells = kChunk / 2;           // cells per dequant workgroup
+constexpr int kHalfCells = kChunk / 2;           // cells per PV k-step
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) const half8_t lds_half8_t;
@@ -156,55 +157,67 @@ __host__ __device__ constexpr int vslot_cell(int j, int e) {
 }  // namespace
 
 // ---------------------------------------------------------------- dequant
-// One workgroup per (group, chunk, 32-cell half).  Every thread loads 16
-// consecutive codes (a cell row is 16 lanes x 16 bytes) and the scale of two
-// cells, for K and for V; K goes straight to its image, V is transposed
-// through LDS so that each thread then writes one dim's four slot groups.
+// One workgroup per (group, chunk, 32-cell half kk); wave j takes V^T slot
+// group 4 kk + j, i.e. the eight cells 32 kk + 16 (e / 4) + 4 j + e % 4
+// (e < 8) that fill one 16-byte slot group of every V^T row.  Lane i
+// converts dims 4 i .. 4 i + 3 of those cells' V codes (one 4-byte load per
+// cell) and writes the four slot groups; for K, lane i converts 32 dims of
+// cell e = i / 8 and writes its four 16-byte groups.  Every load is issued
+// before any use, and no LDS or barrier is needed; the four waves together
+// write whole 64-byte pieces of each V^T row.
 __global__ __launch_bounds__(256) void dequant_chunks_kernel(RowArgs a, int n_needed,
                                                              int nchunks, uint8_t* ws) {
-  __shared__ _Float16 vt[kHeadDim][kHalfCells + 2];  // [dim][cell], padded rows
-  const int tid = threadIdx.x;
-  const int kk = blockIdx.x & 1;  // 32-cell half of the chunk
+  const int lane = threadIdx.x & 63;
+  const int kk = blockIdx.x & 1, j = threadIdx.x >> 6;
+  const int u = 4 * kk + j;        // slot group
   const int gk = blockIdx.x >> 1;  // (group, chunk)
   const int g = gk / nchunks, k = gk % nchunks;
-  const int cb = k * kChunk + kHalfCells * kk;
   uint8_t* img = ws + (int64_t)gk * kImg;
-  const int seg = tid & 15;  // dims 16 seg .. +15
-  auto code = [](const u32x4& raw, int byte) -> _Float16 {
-    return (_Float16)(int8_t)(raw[byte >> 2] >> (8 * (byte & 3)));
-  };
+  const int64_t gbase = (int64_t)g * a.n_cells;
+  auto cell_of = [&](int e) { return kHalfCells * kk + vslot_cell(j, e); };  // inside the chunk
+
+  // ---- V: dims 4 lane .. +3 of the eight cells
+  uint32_t vraw[8];
+  uint16_t vbits[8];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int c = (tid >> 4) + 16 * r;  // cell cb + c
-    const int cell = cb + c;
+  for (int e = 0; e < 8; ++e) {
+    const int cell = k * kChunk + cell_of(e);
     const bool live = cell < n_needed;
-    const int64_t row = ((int64_t)g * a.n_cells + (live ? cell : 0)) * kHeadDim + 16 * seg;
-    const int64_t srow = ((int64_t)g * a.n_cells + (live ? cell : 0)) * kNBlk + (seg >> 2);
-    const u32x4 kraw = *reinterpret_cast<const u32x4*>(a.kq + row);
-    const u32x4 vraw = *reinterpret_cast<const u32x4*>(a.vq + row);
-    // cells past the last visible one are zero
-    const uint16_t kbits = live ? reinterpret_cast<const uint16_t*>(a.ksc)[srow] : (uint16_t)0;
-    const uint16_t vbits = live ? reinterpret_cast<const uint16_t*>(a.vsc)[srow] : (uint16_t)0;
-    const _Float16 ks = __builtin_bit_cast(_Float16, kbits);
-    const _Float16 vs = __builtin_bit_cast(_Float16, vbits);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      half8_t v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = code(kraw, 8 * half + e) * ks;
-      *reinterpret_cast<half8_t*>(img + kimg_off(kHalfCells * kk + c, 2 * seg + half)) = v;
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) vt[16 * seg + e][c] = code(vraw, e) * vs;
+    const int64_t row = gbase + (live ? cell : 0);
+    vraw[e] = *reinterpret_cast<const uint32_t*>(a.vq + row * kHeadDim + 4 * lane);
+    vbits[e] = live ? reinterpret_cast<const uint16_t*>(a.vsc)[row * kNBlk + (lane >> 4)]
+                    : (uint16_t)0;
   }
-  __syncthreads();
-  const int d = tid;
+  // ---- K: cell e = lane / 8, dims 32 (lane % 8) .. +31
+  const int ke = lane >> 3, kseg = lane & 7;
+  const int kc = cell_of(ke);
+  const int kcell = k * kChunk + kc;
+  const bool klive = kcell < n_needed;
+  const int64_t krow = gbase + (klive ? kcell : 0);
+  const u32x4 k0 = *reinterpret_cast<const u32x4*>(a.kq + krow * kHeadDim + 32 * kseg);
+  const u32x4 k1 = *reinterpret_cast<const u32x4*>(a.kq + krow * kHeadDim + 32 * kseg + 16);
+  const uint16_t kbits =
+      klive ? reinterpret_cast<const uint16_t*>(a.ksc)[krow * kNBlk + (kseg >> 1)] : (uint16_t)0;
+
+  auto code = [](uint32_t w, int byte) -> _Float16 { return (_Float16)(int8_t)(w >> (8 * byte)); };
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int m = 0; m < 4; ++m) {
     half8_t v;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = vt[d][vslot_cell(j, e)];
-    *reinterpret_cast<half8_t*>(img + kHalf + vimg_off(d, 4 * kk + j)) = v;
+    for (int e = 0; e < 8; ++e) v[e] = code(vraw[e], m) * __builtin_bit_cast(_Float16, vbits[e]);
+    *reinterpret_cast<half8_t*>(img + kHalf + vimg_off(4 * lane + m, u)) = v;
+  }
+  const _Float16 ks = __builtin_bit_cast(_Float16, kbits);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t w0 = (h < 2 ? k0 : k1)[2 * (h & 1)], w1 = (h < 2 ? k0 : k1)[2 * (h & 1) + 1];
+    half8_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = code(w0, e) * ks;
+      v[4 + e] = code(w1, e) * ks;
+    }
+    *reinterpret_cast<half8_t*>(img + kimg_off(kc, 4 * kseg + h)) = v;
   }
 }
 
