@@ -31,7 +31,10 @@
 //   flash_tile_kernel  one workgroup per (group, 10 tokens): 120 queries
 //     (10 tokens x 12 heads) on 8 waves x 16 query slots, two waves per
 //     SIMD, so that one wave's softmax runs on the VALU while the other's
-//     products occupy the matrix core.  Products on v_mfma_f32_16x16x32_f16
+//     products occupy the matrix core.  When that grid would not cover the
+//     256 CUs (short prompts), workgroups of 4 waves take 5 tokens each:
+//     twice the workgroups, each running its chunks about twice as fast on
+//     one wave per SIMD.  Products on v_mfma_f32_16x16x32_f16
 //     with queries in the N dimension:
 //       S^T[64 cells][16 queries] = K Q^T   (A = K from LDS, B = Q^T held in
 //                                            registers for the whole block)
@@ -68,14 +71,15 @@ namespace qsa {
 
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kQpw = 16;                    // query slots per wave
-constexpr int kSlots = kQpw * kWaves;       // query slots per workgroup
-constexpr int kTileTokens = kSlots / kHpg;  // whole tokens per workgroup (10)
+constexpr int kQpw = 16;  // query slots per wave
+// Whole tokens per workgroup of `waves` waves: 10 with 8 waves, 5 with 4.
+__host__ __device__ constexpr int tile_tokens(int waves) { return kQpw * waves / kHpg; }
+// MI355X compute units: below this many 8-wave workgroups the grid would
+// leave CUs idle, and 4-wave workgroups of half as many tokens are used.
+constexpr int kCus = 256;
 constexpr float kP16Max = 65504.0f;         // largest finite fp16
 constexpr int kHalf = kChunk * kHeadDim * 2;  // bytes of one K or V^T image (32 KB)
 constexpr int kImg = 2 * kHalf;               // bytes per (group, chunk) in the workspace
-constexpr int kCopyOps = kHalf / 1024 / kWaves;  // 1 KB copies per wave per image (4)
 constexpr int kHalfCells = kChunk / 2;           // cells per PV k-step
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -222,9 +226,12 @@ __global__ __launch_bounds__(256) void dequant_chunks_kernel(RowArgs a, int n_ne
 }
 
 // ---------------------------------------------------------------- attention
+template <int kWaves>
 __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, int t_count,
                                                                     int nchunks,
                                                                     const uint8_t* ws) {
+  constexpr int kTileTokens = tile_tokens(kWaves);
+  constexpr int kCopyOps = kHalf / 1024 / kWaves;  // 1 KB copies per wave per image
   // K(c) lives in kv[c & 1], V^T(c) in kv[2 + (c & 1)]
   __shared__ __attribute__((aligned(16))) uint8_t kv[4 * kHalf];
   __shared__ int s_redo;  // set when the fast pass must be redone exactly
@@ -567,9 +574,16 @@ hipError_t launch_tile_attend(const RowArgs& a, int t_count, const void* ws, hip
   if (t_count <= 0) return hipSuccess;
   const int n_needed = a.pos0 + t_count;
   const int nchunks = (n_needed + kChunk - 1) / kChunk;
-  const int n_blocks = (t_count + kTileTokens - 1) / kTileTokens;
-  flash_tile_kernel<<<dim3(n_blocks * a.G), dim3(kWaves * 64), 0, stream>>>(
-      a, t_count, nchunks, static_cast<const uint8_t*>(ws));
+  const uint8_t* img = static_cast<const uint8_t*>(ws);
+  const int blocks8 = (t_count + tile_tokens(8) - 1) / tile_tokens(8);
+  if (blocks8 * a.G >= kCus) {
+    flash_tile_kernel<8><<<dim3(blocks8 * a.G), dim3(8 * 64), 0, stream>>>(a, t_count, nchunks,
+                                                                             img);
+  } else {
+    const int blocks4 = (t_count + tile_tokens(4) - 1) / tile_tokens(4);
+    flash_tile_kernel<4><<<dim3(blocks4 * a.G), dim3(4 * 64), 0, stream>>>(a, t_count, nchunks,
+                                                                             img);
+  }
   return hipGetLastError();
 }
 

@@ -121,6 +121,24 @@ def test_scores_growing_after_the_first_chunk(late_scale):
     _check(gpu_flash(inp), ref)
 
 
+@pytest.mark.parametrize("T,late_scale", [(1000, None), (1000, 0.5), (1300, None), (1300, 0.5)])
+def test_both_tile_widths_sampled_tokens(T, late_scale):
+    # prompts under budget run 8-wave workgroups of 10 tokens when that
+    # grid covers the 256 CUs (2 groups x 130 blocks at T=1300) and 4-wave
+    # workgroups of 5 tokens otherwise (T=1000); late_scale 0.5 makes later
+    # chunks outgrow chunk 0's reference, so the exact rescaling pass runs
+    inp = qsa_synth.layer_inputs(T, 0, seed=17)
+    if late_scale is not None:
+        inp.ksc[:, 64:] = np.float16(late_scale)
+    got = gpu_flash(inp)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(T)
+    toks = sorted(set([0, 4, 5, 9, 10, 63, 64, T // 2, T - 6, T - 5, T - 1]
+                      + rng.integers(0, T, 6).tolist()))
+    for t, sub in _sub_inputs(inp, toks):
+        _check(got[t:t + 1], oracle.attend(sub, None))
+
+
 def test_single_cell_token_returns_its_value():
     inp = qsa_synth.layer_inputs(1, 0, seed=21)
     got = gpu_flash(inp)
