@@ -15,12 +15,15 @@
 //
 //   topk_regs_kernel (rows of at most 512 x 64 cells): the row is read from
 //     HBM once, coalesced, into registers (EPT keys per thread).  A sample
-//     of 1024 keys gives a threshold that leaves, as a rule, a few thousand
-//     keys at or above it; those are counted exactly and copied to an LDS
-//     list, and three radix passes of 11, 11 and 10 bits (LDS atomics) run
-//     over the list alone.  When the list would not hold budget..6144 keys,
-//     the passes run over the registers instead (every key in the first
-//     pass, then only keys that match the prefix found so far).  The selection is then two LDS bitmaps over
+//     of 1024 evenly spaced cells gives a threshold that leaves, as a rule,
+//     a few thousand keys at or above it; those are counted exactly and
+//     copied to an LDS list, and three radix passes of 11, 11 and 10 bits
+//     (LDS atomics) run over the list alone.  When the list would not hold
+//     budget..6144 keys, the passes run over the registers instead (every
+//     key in the first pass, then only keys that match the prefix found so
+//     far).  Each pass's digit search zeroes the bins it reads, and its
+//     scans alternate between two buffers, so a pass costs two barriers and
+//     no separate clearing.  The selection is then two LDS bitmaps over
 //     the row's cells (key > K, key == K), built from one ballot per 64
 //     cells, and two block-wide scans over the bitmap words: the first keeps
 //     the first krem equal keys, the second gives every selected cell its
@@ -80,6 +83,25 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wsum, u
   return base + incl - v;
 }
 
+// The same with one barrier: the caller alternates between two `wsum`
+// buffers, so a buffer is rewritten only two calls later, after the middle
+// call's barrier has passed every read of it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_sum1(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int w = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_sum(v);
+  if ((threadIdx.x & 63) == 63) wsum[w] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t c = wsum[i];
+    base += (i < w) ? c : 0u;
+    tot += c;
+  }
+  total = tot;
+  return base + incl - v;
+}
 
 // Identity row: 0 .. n-1, then -1 padding.
 __device__ __forceinline__ void write_identity(int32_t* out, int64_t n, int budget, int nt) {
@@ -105,12 +127,12 @@ topk_regs_kernel(const float* __restrict__ scores,
   // hist[0] serves every pass; in the first pass hist[1..3] are extra copies
   // (one per 16-lane quarter of a wave, fewer same-bin atomic collisions),
   // afterwards their space holds the survivors of the first digit
-  __shared__ uint32_t hist[4][2048];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][2048];
   uint32_t* const list = &hist[1][0];
   static_assert(3 * 2048 >= kListCap, "survivor list fits in hist[1..3]");
   __shared__ __attribute__((aligned(8))) uint32_t bm_gt[kWords], bm_eq[kWords];  // key > K (or >=), == K
-  __shared__ uint32_t wsum[NW], wcount[NW];
-  __shared__ uint32_t s_digit, s_above, s_count;
+  __shared__ uint32_t wsum[2][NW], wcount[NW];
+  __shared__ uint32_t s_digit[2], s_above[2], s_count[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = blockIdx.x;  // t * G + g
   const int64_t n = (int64_t)pos0 + row / G + 1;
@@ -142,35 +164,52 @@ topk_regs_kernel(const float* __restrict__ scores,
   // ---- radix select, most significant digit first.  The block finds the
   // digit of the krem-th largest remaining key from a histogram `h`.
   uint32_t prefix = 0, krem = (uint32_t)budget, eq_count = 0;
+  int parity = 0;  // alternates the scan and result buffers between calls
+  auto excl_sum = [&](uint32_t v, uint32_t& total) {
+    parity ^= 1;
+    return block_excl_sum1<NT>(v, wsum[parity], total);
+  };
+  // The bins it reads are zeroed on the way (each thread owns its four), so
+  // the next histogram starts from zero after the barrier inside.
   auto choose = [&](int shift, bool four_copies) {
     // bins in descending order: thread tid owns bins 2047 - 4 tid - q, q < 4
+    // (one 16-byte word: element 3 - q)
+    const int b0 = 2044 - 4 * tid;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 h = *reinterpret_cast<const u32x4*>(&hist[0][b0]);
+    *reinterpret_cast<u32x4*>(&hist[0][b0]) = zero;
+    if (four_copies) {
+#pragma unroll
+      for (int cp = 1; cp < 4; ++cp) {
+        h += *reinterpret_cast<const u32x4*>(&hist[cp][b0]);
+        *reinterpret_cast<u32x4*>(&hist[cp][b0]) = zero;
+      }
+    }
     uint32_t c[4], mine = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int b = 2047 - 4 * tid - q;
-      c[q] = hist[0][b];
-      if (four_copies) c[q] += hist[1][b] + hist[2][b] + hist[3][b];
+      c[q] = h[3 - q];
       mine += c[q];
     }
     uint32_t total;
-    const uint32_t excl = block_excl_sum<NT>(mine, wsum, total);
+    const uint32_t excl = excl_sum(mine, total);
+    const int p = parity;
     if (excl < krem && krem <= excl + mine) {  // exactly one thread
       uint32_t acc = excl;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (acc < krem && krem <= acc + c[q]) {
-          s_digit = 2047u - 4u * tid - q;
-          s_above = acc;
-          s_count = c[q];
+          s_digit[p] = 4u * tid + q;  // 2047 - digit
+          s_above[p] = acc;
+          s_count[p] = c[q];
         }
         acc += c[q];
       }
     }
     __syncthreads();
-    prefix |= s_digit << shift;
-    krem -= s_above;
-    eq_count = s_count;
-    __syncthreads();  // everyone has read s_* before they are rewritten
+    prefix |= (2047u - s_digit[p]) << shift;
+    krem -= s_above[p];
+    eq_count = s_count[p];
   };
   auto clear_hist = [&](int words) {
     for (int b = tid; b < words; b += NT) (&hist[0][0])[b] = 0u;
@@ -185,8 +224,8 @@ topk_regs_kernel(const float* __restrict__ scores,
       key[i] = tid < n32 - NT * i ? key[i] : 0u;
   }
 
-  // ---- a threshold from a sample.  Every thread draws two keys from the
-  // row's live slots; the digit (bits 31..21) of the sample's r-th largest
+  // ---- a threshold from a sample.  Every thread reads two evenly spaced
+  // cells of the row; the digit (bits 31..21) of the sample's r-th largest
   // key, r set four standard deviations above the sample's expected count
   // of selected cells, gives t = digit << 21, which usually leaves between
   // budget and kListCap keys at or above it.  Those keys go to the list and
@@ -195,17 +234,15 @@ topk_regs_kernel(const float* __restrict__ scores,
   // least budget keys).  Otherwise the full passes below run.
   bool listed = false;
   {
-    const int live_slots = (n32 + NT - 1) / NT;
+    // cells (2 tid + sm) n / (2 NT) of the row, spread over it (read again,
+    // from L2, while the histogram is cleared)
     uint32_t smp[2];
 #pragma unroll
-    for (int sm = 0; sm < 2; ++sm) {
-      const int target = (tid * 37 + sm * 13 + 7) % live_slots;
-      uint32_t v = 0u;
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) v = (i == target) ? key[i] : v;
-      smp[sm] = v;
-    }
+    for (int sm = 0; sm < 2; ++sm)
+      smp[sm] = __float_as_uint(srow[(uint32_t)(2 * tid + sm) * (uint32_t)n32 / (2 * NT)]);
     clear_hist(2048);
+#pragma unroll
+    for (int sm = 0; sm < 2; ++sm) smp[sm] = score_key(__uint_as_float(smp[sm]));
     atomicAdd(&hist[0][smp[0] >> 21], 1u);
     atomicAdd(&hist[0][smp[1] >> 21], 1u);
     __syncthreads();
@@ -220,24 +257,22 @@ topk_regs_kernel(const float* __restrict__ scores,
 #pragma unroll
     for (int i = 0; i < EPT; ++i) mine += key[i] >= t ? 1u : 0u;
     uint32_t n_at;
-    uint32_t pos = block_excl_sum<NT>(mine, wsum, n_at);
+    uint32_t pos = excl_sum(mine, n_at);
     if (n_at >= (uint32_t)budget && n_at <= (uint32_t)kListCap) {
       listed = true;
 #pragma unroll
       for (int i = 0; i < EPT; ++i)
         if (key[i] >= t) list[pos++] = key[i];
-      clear_hist(2048);  // (its barrier also publishes the list)
+      __syncthreads();  // publishes the list (hist[0] is zero: choose cleared it)
       for (int j = tid; j < (int)n_at; j += NT) atomicAdd(&hist[0][list[j] >> 21], 1u);
       __syncthreads();
       choose(21, false);
-      clear_hist(2048);
       for (int j = tid; j < (int)n_at; j += NT) {
         const uint32_t k = list[j];
         if ((k >> 21) == (prefix >> 21)) atomicAdd(&hist[0][(k >> 10) & 0x7ffu], 1u);
       }
       __syncthreads();
       choose(10, false);
-      clear_hist(2048);
       for (int j = tid; j < (int)n_at; j += NT) {
         const uint32_t k = list[j];
         if ((k >> 10) == (prefix >> 10)) atomicAdd(&hist[0][k & 0x3ffu], 1u);
@@ -269,7 +304,7 @@ topk_regs_kernel(const float* __restrict__ scores,
 #pragma unroll
     for (int i = 0; i < EPT; ++i) cnt += __popcll(__ballot((key[i] >> 21) == d1));
     if (lane == 0) wcount[w] = cnt;
-    clear_hist(2048);  // (its barrier also publishes wcount)
+    __syncthreads();  // publishes wcount
     uint32_t pos = 0;
     for (int v = 0; v < w; ++v) pos += wcount[v];
 #pragma unroll
@@ -286,7 +321,6 @@ topk_regs_kernel(const float* __restrict__ scores,
     for (int j = tid; j < (int)n1; j += NT) atomicAdd(&hist[0][(list[j] >> 10) & 0x7ffu], 1u);
     __syncthreads();
     choose(10, false);
-    clear_hist(2048);
     for (int j = tid; j < (int)n1; j += NT) {
       const uint32_t k = list[j];
       if ((k >> 10) == (prefix >> 10)) atomicAdd(&hist[0][k & 0x3ffu], 1u);
@@ -295,13 +329,11 @@ topk_regs_kernel(const float* __restrict__ scores,
     choose(0, false);
   } else {
     // too many survivors for the list: the same two digits over the registers
-    clear_hist(2048);
 #pragma unroll
     for (int i = 0; i < EPT; ++i)
       if ((key[i] >> 21) == d1) atomicAdd(&hist[0][(key[i] >> 10) & 0x7ffu], 1u);
     __syncthreads();
     choose(10, false);
-    clear_hist(2048);
 #pragma unroll
     for (int i = 0; i < EPT; ++i)
       if ((key[i] >> 10) == (prefix >> 10)) atomicAdd(&hist[0][key[i] & 0x3ffu], 1u);
@@ -352,7 +384,7 @@ topk_regs_kernel(const float* __restrict__ scores,
       n_eq += wd < kWords ? __popc(bm_eq[wd]) : 0u;
     }
     uint32_t eq_total;
-    uint32_t rank = block_excl_sum<NT>(n_eq, wsum, eq_total);
+    uint32_t rank = excl_sum(n_eq, eq_total);
 #pragma unroll
     for (int k = 0; k < kWpt; ++k) {
       const int wd = kWpt * tid + k;
@@ -369,7 +401,7 @@ topk_regs_kernel(const float* __restrict__ scores,
 #pragma unroll
   for (int k = 0; k < kWpt; ++k) n_sel += __popc(sel[k]);
   uint32_t sel_total;
-  uint32_t pos = block_excl_sum<NT>(n_sel, wsum, sel_total);  // sel_total == budget
+  uint32_t pos = excl_sum(n_sel, sel_total);  // sel_total == budget
 #pragma unroll
   for (int k = 0; k < kWpt; ++k) {
     uint32_t b = sel[k];
