@@ -20,6 +20,10 @@ Other workloads (--workload):
                                   cells) + qsa_flash with explicit ids;
   decode4_pos8192                 4 tokens at position 8192: qsa_topk,
                                   split qsa_flash, qsa_merge;
+  t1984_pos30000_split            the long-context prompt through the same
+                                  split path (one wavefront per selected
+                                  64-cell chunk, then the merge) instead
+                                  of the fused row kernel;
   quantize_kv_31984               the K/V quantiser on the long-context
                                   cache: qsa_quantize of the fp16 K and V
                                   rows of 2 groups x 31,984 cells per step
@@ -79,7 +83,8 @@ WORKLOADS = {
     "t1024_pos0_x12": dict(T=1024, pos0=0, layers=12, kind="prompt"),
     "t512_pos0_x12": dict(T=512, pos0=0, layers=12, kind="prompt"),
     "t1984_pos30000": dict(T=1984, pos0=30000, layers=1, kind="prompt"),
-    "decode4_pos8192": dict(T=4, pos0=8192, layers=1, kind="decode"),
+    "decode4_pos8192": dict(T=4, pos0=8192, layers=1, kind="split"),
+    "t1984_pos30000_split": dict(T=1984, pos0=30000, layers=1, kind="split"),
     "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
 }
 AUTO_WARMUP_S = 0.3  # default warmup: the GPU clock takes tens of ms under load to settle
@@ -252,7 +257,7 @@ def main():
         if inp.scores is not None:
             d["ids"] = torch.empty((T, 2, inp.budget), dtype=torch.int32, device=dev)
         d["out"] = torch.empty((T, s.n_heads, 256), dtype=torch.float16, device=dev)
-        if kind == "decode":
+        if kind == "split":
             d["part"] = torch.empty((T, s.n_part_chunks, s.n_heads, qsa.PART_STRIDE),
                                     dtype=torch.float32, device=dev)
         d["shape"] = s
@@ -269,7 +274,7 @@ def main():
             s = d["shape"]
             if d["scores"] is not None:
                 qsa.qsa_topk(s, d["scores"], d["ids"])
-            if kind == "decode":
+            if kind == "split":
                 qsa.qsa_flash(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"], None,
                               d["part"])
                 qsa.qsa_merge(s, d["part"], d["out"])
@@ -278,24 +283,27 @@ def main():
                 qsa.qsa_flash_attend(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"],
                                      d["out"], workspace=ws)
 
+    repeat = DECODE_REPEAT if T <= 8 else 1
+
     def step_timed(ev0, ev1) -> int:
         """The same step with its dominant launches back to back between two
         events: every layer is prepared (into its own workspace) before the
         attend launches run; a decode step's split qsa_flash call, which
-        only rewrites its partials, runs DECODE_REPEAT times.  Returns the
-        number of launches between the events."""
-        if kind == "decode":
+        only rewrites its partials, runs DECODE_REPEAT times (once for
+        prompt-sized splits).  Returns the number of launches between the
+        events."""
+        if kind == "split":
             for d in layers:
                 qsa.qsa_topk(d["shape"], d["scores"], d["ids"])
             ev0.record()
-            for _ in range(DECODE_REPEAT):
+            for _ in range(repeat):
                 for d in layers:
                     qsa.qsa_flash(d["shape"], d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"],
                                   d["ids"], None, d["part"])
             ev1.record()
             for d in layers:
                 qsa.qsa_merge(d["shape"], d["part"], d["out"])
-            return DECODE_REPEAT * L
+            return repeat * L
         for d in layers:
             s = d["shape"]
             if d["scores"] is not None:
@@ -353,12 +361,17 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                    "kernel": ("flash_rows_kernel<true> (split qsa_flash)" if kind == "decode"
+                    "kernel": ("flash_rows_kernel<true> (split qsa_flash)" if kind == "split"
                                else "flash_rows_kernel<false> (qsa_flash_attend)"),
                     "algorithmic_bytes_per_launch": by, "mean_launch_us": mean_launch_s * 1e6,
                     "launch_timing": LAUNCH_TIMING}
+        if kind == "split":
+            # the (o, m, l) records the split call writes (and the merge
+            # reads): one per (token, selected 64-cell chunk, head)
+            n_rec = sum(-(-min(pos0 + t + 1, budget) // 64) for t in range(T)) * 2 * 12
+            roofline["partial_bytes_per_launch"] = n_rec * qsa.PART_STRIDE * 4
     m5 = PAGES_M5_TOKS.get(T) if (pos0 == 0 and L == 12) else None
-    steps_desc = {"prompt": "qsa_flash", "decode": "qsa_topk + split qsa_flash + qsa_merge"}
+    steps_desc = {"prompt": "qsa_flash", "split": "qsa_topk + split qsa_flash + qsa_merge"}
     line = {
         "metric": "qsa_flash query-tokens/s at T=%d (%d layer%s)" % (T, L, "s" if L > 1 else ""),
         "value": value,
