@@ -57,8 +57,13 @@
 //     at most l (their fp32 sum), so l < 65504 at the end proves that no P
 //     overflowed fp16.  Otherwise (rare: scores far above chunk 0's) the
 //     workgroup votes to recompute the block by an exact online-softmax
-//     pass that moves the running max and rescales O.  Either way the result
+//     pass that moves the running max and rescales O (one chunk per step,
+//     no overlap: it is rare, and lean in registers).  Either way the result
 //     after the final division by l is the same softmax.
+//
+//     Output.  The fast pass stages each wave's O^T tile, as fp16 rows, in
+//     the idle chunk buffers and writes it with 16-byte stores, two whole
+//     512-byte output rows per store instruction.
 //
 // Workgroup i takes KV group i % G; with G = 2 and workgroups dealt to the
 // 8 XCDs round robin, each XCD's L2 holds one group's images only.
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     constexpr int KP = decltype(KP_T)::value;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) sacc[mt] = zero4();
+    // (fences: the scheduler would hoist every fragment read; registers)
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -310,6 +316,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
             lds16(koff[s & 3] + (KP * kHalf + 256 * (s >> 2) + mt * 16 * (kHeadDim * 2)));
         sacc[mt] = mfma16(af, qf[s], sacc[mt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -358,18 +365,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   // O^T += V^T P^T for the chunk whose V^T image sits in kv[2 + VP]
   auto pv = [&](auto VP_T, const half8_t (&pb)[2], f32x4 (&oacc)[16]) {
     constexpr int VP = decltype(VP_T)::value;
+    // (fences every four fragments, as in scores)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
         const half8_t af = lds16(voff[kk] + (VP * kHalf + mt * 16 * (kChunk * 2)));
         oacc[mt] = mfma16(af, pb[kk], oacc[mt]);
+        if ((mt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
   };
 
   // One pass over the block's chunks; returns true when the fast pass must
-  // be redone exactly (SAFE = false only).
-  auto run = [&](auto SAFE_T, bool prefetched) -> bool {
+  // be redone exactly (SAFE = false only).  The fast pass finds its first
+  // chunk images (and K of the second) already requested.
+  auto run = [&](auto SAFE_T) -> bool {
     constexpr bool SAFE = decltype(SAFE_T)::value;
     f32x4 oacc[16];
 #pragma unroll
@@ -377,26 +387,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     float m_ref = -INFINITY, l_run = 0.f;
     bool over = false;
 
-    if (!prefetched) {
-      copy_k(0);
-      copy_v(0);
-      if (nch > 1) copy_k(1);
-    }
-    wait_vmcnt0();
-    wg_barrier();
-    f32x4 s_cur[4];
-    scores(std::integral_constant<int, 0>{}, s_cur);
-
-    // chunk c (parity P): (NEXT) the scores of c + 1, the softmax of c, PV of c
-    auto step = [&](int c, auto NEXT_T, auto P_T) {
-      constexpr bool NEXT = decltype(NEXT_T)::value;
+    // Exact pass, chunk c (parity P), one step at a time: K(c + 1) and
+    // V(c + 1) load while chunk c's scores, online softmax and PV run.
+    auto step = [&](int c, auto P_T) {
       constexpr int P = decltype(P_T)::value;
-      wait_vmcnt0();  // this wave's copies of K(c+1) and V(c) have landed
-      wg_barrier();   // ... every wave's; and nobody reads K(c) or V(c-1) any more
-      if (c + 2 < nch) copy_k(c + 2);
-      if (c + 1 < nch) copy_v(c + 1);
-      f32x4 s_nxt[4];
-      if constexpr (NEXT) scores(std::integral_constant<int, 1 - P>{}, s_nxt);
+      wait_vmcnt0();  // this wave's copies of K(c) and V(c) have landed
+      wg_barrier();   // ... every wave's; and nobody reads chunk c - 1 any more
+      if (c + 1 < nch) {
+        copy_k(c + 1);
+        copy_v(c + 1);
+      }
+      f32x4 s_cur[4];
+      scores(std::integral_constant<int, P>{}, s_cur);
       mask(c, s_cur);
       const float cm = chunk_max(s_cur);
       // exact online softmax (this step serves the exact pass only)
@@ -411,19 +413,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       half8_t pb[2];
       probs(s_cur, m_ref, l_run, pb);
       pv(std::integral_constant<int, P>{}, pb, oacc);
-      if constexpr (NEXT) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) s_cur[mt] = s_nxt[mt];
-      }
     };
     // The same chunk for the fast pass, as an explicit schedule of stages
     // of four MFMAs: the operand fragments of stage i + kAhead are read
     // while stage i multiplies, the softmax exponentials of chunk c are spread
     // over the score stages, and scheduler fences keep that order.
     // Every chunk runs the same body, so the buffer parity is a run-time
-    // offset and the last chunk's score stages multiply a stale K image (in
-    // bounds, untouched by copies) whose result is dropped.
-    auto step_fast = [&](int c, f32x4 (&s_cur)[4], f32x4 (&s_nxt)[4]) {
+    // offset; the last chunk (LAST) has no next chunk to score, and its score
+    // stages only compute the exponentials.
+    auto step_fast = [&](int c, f32x4 (&s_cur)[4], f32x4 (&s_nxt)[4], auto LAST_T) {
+      constexpr bool LAST = decltype(LAST_T)::value;
       constexpr int kS = 8;            // score stages (k-steps of chunk c + 1)
       constexpr int kStages = kS + 8;  // then PV stages: k-step t / 4, m-tiles 4 (t % 4) ..
       constexpr int kAhead = 1;        // stages whose fragments are read ahead
@@ -443,9 +442,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       auto load = [&](auto I, half8_t (&dst)[4]) {
         constexpr int i = decltype(I)::value;
         if constexpr (i < kS) {
+          if constexpr (!LAST) {
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            dst[mt] = lds16(kb[i & 3] + (256 * (i >> 2) + mt * 16 * (kHeadDim * 2)));
+            for (int mt = 0; mt < 4; ++mt)
+              dst[mt] = lds16(kb[i & 3] + (256 * (i >> 2) + mt * 16 * (kHeadDim * 2)));
+          }
         } else {
           constexpr int t = i - kS;
 #pragma unroll
@@ -453,8 +454,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
             dst[m] = lds16(vb[t >> 2] + ((4 * (t & 3) + m) * 16 * (kChunk * 2)));
         }
       };
+      if constexpr (!LAST) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) s_nxt[mt] = zero4();
+        for (int mt = 0; mt < 4; ++mt) s_nxt[mt] = zero4();
+      }
       static_for<kAhead>([&](auto I) { load(I, fr[decltype(I)::value]); });
       // chunk 0 always holds cell 0: the reference is finite
       if (c == 0) m_ref = chunk_max(s_cur);
@@ -478,9 +481,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
         if constexpr (i + kAhead < kStages)
           load(std::integral_constant<int, i + kAhead>{}, fr[(i + kAhead) % (kAhead + 1)]);
         if constexpr (i < kS) {
+          if constexpr (!LAST) {
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            s_nxt[mt] = mfma16(fr[i % (kAhead + 1)][mt], qf[i], s_nxt[mt]);
+            for (int mt = 0; mt < 4; ++mt)
+              s_nxt[mt] = mfma16(fr[i % (kAhead + 1)][mt], qf[i], s_nxt[mt]);
+          }
           expo2(i);
         } else {
           constexpr int t = i - kS;
@@ -497,26 +502,32 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     if constexpr (SAFE) {
+      copy_k(0);
+      copy_v(0);
       int c = 0;
-      for (; c + 2 < nch; c += 2) {
-        step(c, T_{}, P0{});
-        step(c + 1, T_{}, P1{});
+      for (; c + 1 < nch; c += 2) {
+        step(c, P0{});
+        step(c + 1, P1{});
       }
-      if (c + 1 < nch) {
-        step(c, T_{}, P0{});
-        step(c + 1, F_{}, P1{});
-      } else {
-        step(c, F_{}, P0{});
-      }
+      if (c < nch) step(c, P0{});
     } else {
+      wait_vmcnt0();
+      wg_barrier();
+      f32x4 s_cur[4];
+      scores(std::integral_constant<int, 0>{}, s_cur);
       // two chunks per trip: the score registers trade roles, no copies
       f32x4 s_alt[4];
       int c = 0;
-      for (; c + 1 < nch; c += 2) {
-        step_fast(c, s_cur, s_alt);
-        step_fast(c + 1, s_alt, s_cur);
+      for (; c + 2 < nch; c += 2) {
+        step_fast(c, s_cur, s_alt, F_{});
+        step_fast(c + 1, s_alt, s_cur, F_{});
       }
-      if (c < nch) step_fast(c, s_cur, s_alt);
+      if (c + 1 < nch) {
+        step_fast(c, s_cur, s_alt, F_{});
+        step_fast(c + 1, s_alt, s_cur, T_{});
+      } else {
+        step_fast(c, s_cur, s_alt, T_{});
+      }
     }
 
     // ---- finalise: O / l -> fp16; lane (n, j) holds dims 16 mt + 4 j + i
@@ -531,15 +542,42 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       if (s_redo) return true;
     }
 
-    if (qvalid) {
-      const float inv = 1.f / l_tot;
-      _Float16* orow = a.out + ((int64_t)qt * H + qh) * kHeadDim + 4 * j;
+    if constexpr (SAFE) {
+      if (qvalid) {
+        const float inv = 1.f / l_tot;
+        _Float16* orow = a.out + ((int64_t)qt * H + qh) * kHeadDim + 4 * j;
+#pragma unroll
+        for (int mt = 0; mt < 16; ++mt) {
+          half4_t o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = (_Float16)(oacc[mt][i] * inv);
+          *reinterpret_cast<half4_t*>(orow + 16 * mt) = o;
+        }
+      }
+    } else {
+      // O^T goes through LDS (the chunk buffers: every wave is past the
+      // vote's barrier, so none reads them any more) and leaves as 16-byte
+      // stores, two whole output rows per store instruction
+      constexpr int kRowB = kHeadDim * 2 + 16;  // padded row: spreads the banks
+      uint8_t* tile = kv + w * (kQpw * kRowB);
+      const float inv = qvalid ? 1.f / l_tot : 0.f;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
         half4_t o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (_Float16)(oacc[mt][i] * inv);
-        *reinterpret_cast<half4_t*>(orow + 16 * mt) = o;
+        *reinterpret_cast<half4_t*>(tile + n * kRowB + 2 * (16 * mt + 4 * j)) = o;
+      }
+      const int half_row = lane >> 5, seg = lane & 31;
+#pragma unroll
+      for (int r = 0; r < kQpw / 2; ++r) {
+        const int qn = 2 * r + half_row;  // query slot kQpw w + qn
+        const int s2 = kQpw * w + qn;
+        const int t2 = t0 + s2 / kHpg;
+        const half8_t v = *reinterpret_cast<const half8_t*>(tile + qn * kRowB + 16 * seg);
+        if (s2 < kTileTokens * kHpg && t2 <= t_last)
+          *reinterpret_cast<half8_t*>(a.out + ((int64_t)t2 * H + g * kHpg + s2 % kHpg) * kHeadDim +
+                                      8 * seg) = v;
       }
     }
     return false;
@@ -551,7 +589,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   if (tid == 0) s_redo = 0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (run(std::false_type{}, true)) run(std::true_type{}, false);
+  if (run(std::false_type{})) run(std::true_type{});
 }
 
 int64_t tile_workspace_bytes(int G, int t_count, int pos0) {
