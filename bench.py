@@ -19,7 +19,9 @@ Other workloads (--workload):
                                   qsa_topk (top 2051 of up to 31,984
                                   cells) + qsa_flash with explicit ids;
   decode4_pos8192                 4 tokens at position 8192: qsa_topk,
-                                  split qsa_flash, qsa_merge;
+                                  split qsa_flash, qsa_merge (also
+                                  decode1_pos512, decode8_pos2048 and
+                                  decode8_pos30000);
   t1984_pos30000_split            the long-context prompt through the same
                                   split path (one wavefront per selected
                                   64-cell chunk, then the merge) instead
@@ -84,6 +86,9 @@ WORKLOADS = {
     "t512_pos0_x12": dict(T=512, pos0=0, layers=12, kind="prompt"),
     "t1984_pos30000": dict(T=1984, pos0=30000, layers=1, kind="prompt"),
     "decode4_pos8192": dict(T=4, pos0=8192, layers=1, kind="split"),
+    "decode1_pos512": dict(T=1, pos0=512, layers=1, kind="split"),
+    "decode8_pos2048": dict(T=8, pos0=2048, layers=1, kind="split"),
+    "decode8_pos30000": dict(T=8, pos0=30000, layers=1, kind="split"),
     "t1984_pos30000_split": dict(T=1984, pos0=30000, layers=1, kind="split"),
     "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
 }
@@ -294,7 +299,8 @@ def main():
         events."""
         if kind == "split":
             for d in layers:
-                qsa.qsa_topk(d["shape"], d["scores"], d["ids"])
+                if d["scores"] is not None:
+                    qsa.qsa_topk(d["shape"], d["scores"], d["ids"])
             ev0.record()
             for _ in range(repeat):
                 for d in layers:
