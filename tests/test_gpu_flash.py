@@ -259,3 +259,19 @@ def test_other_group_counts(G, T, pos0):
     _check(gpu_flash(inp, ids, dev), ref)
     from gpu_util import gpu_merge
     _check(gpu_merge(inp, gpu_flash(inp, ids, dev, split=True)), ref)
+
+
+@pytest.mark.parametrize("G,T", [(3, 900), (4, 700), (1, 1984)])
+def test_other_group_counts_at_prompt_size(G, T):
+    # prompts long enough for the 8-wave tile kernel (G x ceil(T / 10) of at
+    # least 256 workgroups) with G != 2, and G = 1 on the 4-wave one;
+    # sampled tokens against the oracle
+    inp = qsa_synth.layer_inputs(T, 0, seed=G * 1000 + T, n_groups=G)
+    got = gpu_flash(inp)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(G)
+    for t in sorted(set([0, 9, 10, T // 3, T - 11, T - 10, T - 1] + rng.integers(0, T, 4).tolist())):
+        sub = qsa_synth.LayerInputs(T=1, pos0=t, budget=inp.budget, n_cells=inp.n_cells,
+                                    q=inp.q[t:t + 1], kq=inp.kq, ksc=inp.ksc, vq=inp.vq,
+                                    vsc=inp.vsc, scores=None)
+        _check(got[t:t + 1], oracle.attend(sub, None))
