@@ -487,6 +487,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
               s_nxt[mt] = mfma16(fr[i % (kAhead + 1)][mt], qf[i], s_nxt[mt]);
           }
           expo2(i);
+          if constexpr (!LAST && i + kAhead < kStages) {
+            // inside the stage: one product, one fragment read for the next
+            // stage, one VALU op (the exponentials), four times over
+            static_for<4>([&](auto) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+              __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
+            });
+          }
         } else {
           constexpr int t = i - kS;
 #pragma unroll
