@@ -266,7 +266,10 @@ def main():
             d["part"] = torch.empty((T, s.n_part_chunks, s.n_heads, qsa.PART_STRIDE),
                                     dtype=torch.float32, device=dev)
         d["shape"] = s
-        d["ws"] = qsa.flash_workspace(s, dev)
+        # a workspace of its own per layer (the kernel-timing region
+        # prepares every layer before the attend launches run)
+        need = qsa.qsa_flash_workspace_bytes(s)
+        d["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         layers.append(d)
     # one workspace serves every layer: the calls run in order on one stream
     ws = max((d["ws"] for d in layers if d["ws"] is not None), key=lambda t: t.numel(),
