@@ -275,3 +275,23 @@ def test_other_group_counts_at_prompt_size(G, T):
                                     q=inp.q[t:t + 1], kq=inp.kq, ksc=inp.ksc, vq=inp.vq,
                                     vsc=inp.vsc, scores=None)
         _check(got[t:t + 1], oracle.attend(sub, None))
+
+
+def test_long_prompt_crossing_the_budget_sampled_tokens():
+    # T=4096 at pos0 0: the first 2051 tokens attend every visible cell (the
+    # 8-wave tile kernel over a 33-chunk prefix), the other 2045 their top
+    # 2051 (the row kernel), in one qsa_flash call; sampled tokens on both
+    # sides of the budget against the oracle
+    inp = qsa_synth.layer_inputs(4096, 0, seed=41)
+    dev = upload(inp)
+    gids = gpu_topk(inp, dev)
+    got = gpu_flash(inp, gids, dev)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(4)
+    toks = sorted(set([0, 2049, 2050, 2051, 2052, 4095] + rng.integers(0, 4096, 6).tolist()))
+    for t, sub in _sub_inputs(inp, toks):
+        ids = None
+        if sub.pos0 + 1 > sub.budget:
+            ids = oracle.select(1, sub.pos0, sub.budget, sub.scores, 2, sub.n_cells)
+            np.testing.assert_array_equal(gids[t:t + 1], ids)
+        _check(got[t:t + 1], oracle.attend(sub, ids))
