@@ -502,6 +502,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
           for (int m = 0; m < 4; ++m)
             oacc[4 * (t & 3) + m] =
                 mfma16(fr[i % (kAhead + 1)][m], pb[t >> 2], oacc[4 * (t & 3) + m]);
+          if constexpr (kWaves == 4 && i + kAhead < kStages) {
+            // one wave per SIMD: alternate products and the next stage's
+            // fragment reads (with two waves per SIMD the other wave fills
+            // the gaps, and the scheduler's own order is as fast)
+            static_for<4>([&](auto) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            });
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       });
