@@ -364,7 +364,11 @@ def main():
     if identity_tile:
         roofline = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
-                    "traffic": traffic, "kernel": "flash_tile_kernel (qsa_flash_attend)",
+                    "traffic": traffic,
+                    # the library takes 8-wave workgroups of 10 tokens when at
+                    # least 256 of them cover the prompt, else 4-wave ones of 5
+                    "kernel": "flash_tile_kernel<%d> (qsa_flash_attend)"
+                              % (8 if 2 * -(-T // 10) >= 256 else 4),
                     "flops_per_launch": flops, "mean_launch_us": mean_launch_s * 1e6,
                     "launch_timing": LAUNCH_TIMING}
     else:
