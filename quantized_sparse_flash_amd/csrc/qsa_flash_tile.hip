@@ -49,7 +49,8 @@
 //     score MFMAs before chunk k's softmax, then chunk k's PV.  K and V^T
 //     images have separate double buffers: at chunk k the kernel reads K(k+1)
 //     and V(k) while K(k+2) and V(k+1) stream from L2 into the free halves
-//     (global_load_lds_dwordx4, no registers held).
+//     (global_load_lds_dwordx4, no registers held), issued from inside the
+//     chunk's stage sequence rather than at its start.
 //
 //     Softmax reference.  The first chunk sets each query's reference max
 //     exactly; later chunks keep it, so O is never rescaled.  P = 2^(x - m)
@@ -429,8 +430,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       const uint32_t kpar = ((c + 1) & 1) * kHalf, vpar = (c & 1) * kHalf;
       wait_vmcnt0();  // this wave's copies of K(c+1) and V(c) have landed
       wg_barrier();   // ... every wave's; and nobody reads K(c) or V(c-1) any more
-      if (c + 2 < nch) copy_k(c + 2);
-      if (c + 1 < nch) copy_v(c + 1);
       mask(c, s_cur);
       // the chunk's buffer bases; every fragment is then base + immediate
       uint32_t kb[4], vb[2];
@@ -478,6 +477,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       __builtin_amdgcn_sched_barrier(0);
       static_for<kStages>([&](auto I) {
         constexpr int i = decltype(I)::value;
+        // the next images stream in from inside the stage sequence (K(c+2)
+        // after two score stages, V(c+1) after six), not all at the step's
+        // start: the LDS writes of the copies then interleave with the
+        // fragment reads instead of meeting them in one burst
+        if constexpr (i == 2) {
+          if (c + 2 < nch) copy_k(c + 2);
+        }
+        if constexpr (i == 6) {
+          if (c + 1 < nch) copy_v(c + 1);
+        }
         if constexpr (i + kAhead < kStages)
           load(std::integral_constant<int, i + kAhead>{}, fr[(i + kAhead) % (kAhead + 1)]);
         if constexpr (i < kS) {
