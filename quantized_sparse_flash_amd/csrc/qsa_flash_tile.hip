@@ -477,15 +477,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       __builtin_amdgcn_sched_barrier(0);
       static_for<kStages>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        // the next images stream in from inside the stage sequence (K(c+2)
-        // after two score stages, V(c+1) after six), not all at the step's
-        // start: the LDS writes of the copies then interleave with the
-        // fragment reads instead of meeting them in one burst
-        if constexpr (i == 2) {
-          if (c + 2 < nch) copy_k(c + 2);
-        }
-        if constexpr (i == 6) {
-          if (c + 1 < nch) copy_v(c + 1);
+        // the next images stream in from inside the stage sequence, not all
+        // at the step's start: the LDS writes of the copies then interleave
+        // with the fragment reads instead of meeting them in one burst.
+        // 8 waves: K(c+2) after two score stages, V(c+1) after six; 4 waves
+        // (twice the copies per wave): each image in halves, K after stages
+        // 1 and 3, V after 5 and 7.
+        if constexpr (kWaves == 8) {
+          if constexpr (i == 2) {
+            if (c + 2 < nch) copy_k(c + 2);
+          }
+          if constexpr (i == 6) {
+            if (c + 1 < nch) copy_v(c + 1);
+          }
+        } else if constexpr (i == 1 || i == 3 || i == 5 || i == 7) {
+          constexpr int h = (i == 1 || i == 5) ? 0 : 1;  // first or second half
+          constexpr bool isk = i < 4;
+          const int cc = isk ? c + 2 : c + 1;
+          if (cc < nch) {
+            const uint8_t* src = img_g + (int64_t)cc * kImg + (isk ? 0 : kHalf);
+            const uint32_t dst =
+                lds_addr(kv) + ((isk ? 0 : 2) + (cc & 1)) * kHalf + w * (kHalf / kWaves);
+#pragma unroll
+            for (int op = (kCopyOps / 2) * h; op < (kCopyOps / 2) * (h + 1); ++op)
+              copy16_to_lds(src, copy_voff[op], dst + 1024 * op);
+          }
         }
         if constexpr (i + kAhead < kStages)
           load(std::integral_constant<int, i + kAhead>{}, fr[(i + kAhead) % (kAhead + 1)]);
