@@ -8,13 +8,14 @@ pos0 0 through 12 layers, 2 KV groups x 12 query heads, head dim 256, int8
 K/V codes with fp16 per-64-dim scales, budget 2051.  Every token sees at
 most 1984 cells, so its ids are the identity, derived on the device, and
 the host issues no selection call (the pages' host skips it for such
-prompts); a step is then 12 back-to-back fused qsa_flash calls (each
-enqueued as its two halves, see below), each on its own layer's seeded
-inputs, resident in HBM before the timed region.  The value is query
-tokens per second, T * steps / elapsed.
+prompts); a step is then 12 back-to-back qsa_flash calls, each on its own
+layer's seeded inputs, resident in HBM before the timed region.  The value
+is query tokens per second, T * steps / elapsed.
 
 Other workloads (--workload):
-  t512_pos0_x12, t1024_pos0_x12   the same at T = 512 / 1024;
+  t512_pos0_x12, t1024_pos0_x12   the same at T = 512 / 1024 (the default
+                                  line also carries their figures, under
+                                  "other_prompts");
   t1984_pos30000                  long context: per step one layer of
                                   qsa_topk (top 2051 of up to 31,984
                                   cells) + qsa_flash with explicit ids;
@@ -23,39 +24,37 @@ Other workloads (--workload):
                                   decode1_pos512, decode8_pos2048 and
                                   decode8_pos30000);
   t1984_pos30000_split            the long-context prompt through the same
-                                  split path (one wavefront per selected
-                                  64-cell chunk, then the merge) instead
-                                  of the fused row kernel;
+                                  split path instead of the fused one;
   quantize_kv_31984               the K/V quantiser on the long-context
-                                  cache: qsa_quantize of the fp16 K and V
-                                  rows of 2 groups x 31,984 cells per step
-                                  (cells quantised per second; roofline HBM
-                                  on 512 B in + 264 B out per row).
+                                  cache (cells quantised per second).
 
-One JSON line goes to stdout; progress goes to stderr.  A prompt step
-enqueues each layer's fused qsa_flash as its two halves, qsa_flash_prepare
-(the dequantisation prepass) and qsa_flash_attend.  Without --warmup the
-warmup runs for 0.3 s, long enough for the GPU clock to settle under load
-(with a few steps only it is still rising, and a short timed region reads
-10% slow); without --steps the timed region lasts about 0.2 s (at least 20
-steps).  Two timed regions of K steps follow: the first, with nothing
-between kernels, gives value and ms_per_step; in the second, HIP events on
-the launch stream bracket each step's dominant launches (the attend calls,
-run back to back after every layer is prepared into its own workspace;
-decode: the split qsa_flash call, repeated), for the roofline figures.  An
-event between two kernels costs the stream a few microseconds and would
-count the dispatch of the next kernel as part of it, which is why the
-regions are apart.  The line carries
-  roofline      that kernel against the resource that binds it: for prompt
-                chunks whose tokens are all under budget the tile kernel
-                shares every dequantised chunk among 120 queries, so its
-                bound is fp16 MFMA (algorithmic flops / mean duration);
-                row-gather workloads (tokens above budget, decode) are bound
-                by HBM on the gathered bytes;
-  gathered      algorithmic gathered bytes / the same duration, against the
+One JSON line goes to stdout; progress goes to stderr.  Every C-ABI call of
+a step is bound once (arguments checked and marshalled before timing) and
+then only re-issued.  Without --warmup the warmup runs for 0.3 s, long
+enough for the GPU clock to settle under load; without --steps the timed
+region lasts about 0.2 s (at least 20 steps).  Three timed regions follow:
+  1. K steps back to back, nothing else on the stream: value, ms_per_step;
+  2. the pages' protocol: SAMPLES single steps, each bracketed by HIP
+     events, each preceded (outside the events) by a 1 GiB write that
+     flushes the 256 MB Infinity Cache and the L2s: median and min ms per
+     step ("samples");
+  3. kernel timing, for the roofline: HIP events on the launch stream
+     around K groups of back-to-back qsa_flash calls (one per layer; the
+     whole call, every kernel it enqueues), and for prompts also around the
+     attention kernel alone (every layer prepared first).  An event between
+     two kernels costs the stream a few microseconds, which is why this
+     region is apart from the first.
+The line carries
+  roofline      the qsa_flash call against the resource that binds it: fp16
+                MFMA for prompt chunks (algorithmic flops / mean call
+                duration), HBM for the K/V quantiser; traffic = counter HBM
+                bytes per call from profiles/, null when the kernel sources
+                changed since;
+  attend_only   the attention kernel alone, same units (prompts);
+  gathered      algorithmic gathered bytes / the call duration, against the
                 HBM peak (above 1 when chunks are shared from L2);
-  mfma          algorithmic flops / the same duration;
-  cpu_baseline  the fp64 oracle on this host, a bounded sample.
+  cpu_baseline  the fp64 oracle on this host, a bounded sample, plus one
+                single-thread T=512 layer.
 """
 from __future__ import annotations
 
@@ -63,6 +62,8 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -92,45 +93,18 @@ WORKLOADS = {
     "t1984_pos30000_split": dict(T=1984, pos0=30000, layers=1, kind="split"),
     "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
 }
+# the default line also reports these (12 layers each, same protocol)
+OTHER_PROMPTS = ("t512_pos0_x12", "t1024_pos0_x12")
 AUTO_WARMUP_S = 0.3  # default warmup: the GPU clock takes tens of ms under load to settle
 AUTO_TIMED_S = 0.2    # default timed region length
 MIN_STEPS = 20
-
-
-def run_warmup(args, step, sync):
-    """Runs the warmup steps: exactly args.warmup of them when given, else
-    steps until AUTO_WARMUP_S has passed (at least 3).  Fills in args.warmup
-    and, when not given, args.steps (enough steps for about AUTO_TIMED_S).
-    Returns nothing; the caller's timed regions follow."""
-    t0 = time.perf_counter()
-    n = 0
-    if args.warmup is not None:
-        for _ in range(args.warmup):
-            step()
-        sync()
-        n = args.warmup
-    else:
-        while n < 3 or time.perf_counter() - t0 < AUTO_WARMUP_S:
-            step()
-            n += 1
-            if n % 8 == 0:
-                sync()
-        sync()
-        args.warmup = n
-    if args.steps is None:
-        per_step = (time.perf_counter() - t0) / max(n, 1)
-        args.steps = max(MIN_STEPS, min(5000, int(AUTO_TIMED_S / max(per_step, 1e-6))))
-
+SAMPLES = 30          # single-step samples of the pages' protocol
+FLUSH_BYTES = 1 << 30  # written before each sample: 4x the Infinity Cache
 
 DECODE_REPEAT = 16  # split qsa_flash launches per kernel-timing step (decode)
 QUANT_REPEAT = 8    # K and V qsa_quantize launch pairs per kernel-timing step
-LAUNCH_TIMING = ("HIP events on the launch stream around each step's dominant launches, run "
-                 "back to back (every layer prepared first; decode: the split flash call "
-                 "%d times; quantiser: the step %d times), over a second timed region of K "
-                 "steps; value and ms_per_step come from the first region, which has no "
-                 "events" % (DECODE_REPEAT, QUANT_REPEAT))
 QUANT_ROW_BYTES = 256 * 2 + 256 + 4 * 2  # fp16 row in; int8 codes + 4 fp16 scales out
-# sources of the kernel whose HBM traffic each workload's record describes
+# sources of the kernels whose HBM traffic each workload's record describes
 TRAFFIC_SOURCES = {
     "t1984_pos0_x12": ("qsa_flash_tile.hip", "qsa_device.h"),
     "t1984_pos30000": ("qsa_flash_rows.hip", "qsa_device.h"),
@@ -165,8 +139,9 @@ def kernel_source_hash(names) -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, if it was taken on the current kernel sources; else None."""
+    """HBM bytes per qsa_flash call from the committed rocprofv3 counter
+    summary of this workload, if it was taken on the current kernel
+    sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -179,6 +154,47 @@ def measured_traffic(workload: str):
     if not rec or not names or rec.get("kernel_sources_sha256") != kernel_source_hash(names):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def run_warmup(args, step, sync):
+    """Runs the warmup steps: exactly args.warmup of them when given, else
+    steps until AUTO_WARMUP_S has passed (at least 3).  Returns (warmup
+    steps run, timed steps to use)."""
+    t0 = time.perf_counter()
+    n = 0
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        sync()
+        n = args.warmup
+    else:
+        while n < 3 or time.perf_counter() - t0 < AUTO_WARMUP_S:
+            step()
+            n += 1
+            if n % 8 == 0:
+                sync()
+        sync()
+    steps = args.steps
+    if steps is None:
+        per_step = (time.perf_counter() - t0) / max(n, 1)
+        steps = max(MIN_STEPS, min(5000, int(AUTO_TIMED_S / max(per_step, 1e-6))))
+    return n, steps
+
+
+def single_thread_oracle_t512():
+    """One T=512, pos0 0 layer of the fp64 oracle on one host thread (a child
+    process with OMP_NUM_THREADS=1): seconds and query tokens/s."""
+    code = ("import sys, time; sys.path.insert(0, %r); import oracle, qsa_synth; "
+            "inp = qsa_synth.layer_inputs(512, 0, layer=0); t = time.perf_counter(); "
+            "oracle.attend(inp, None); print(time.perf_counter() - t)" % ROOT)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=600)
+    if r.returncode != 0:
+        return None
+    s = float(r.stdout.strip().splitlines()[-1])
+    return {"value": 512 / s, "unit": "query-tokens/s (1 layer)", "cores": 1, "kind": "oracle",
+            "sample": "one T=512 pos0 0 layer, fp64 oracle attention, one thread, %.2f s" % s}
 
 
 def cpu_baseline(T: int, pos0: int, layers: int, target_s: float = 12.0, max_layers: int = 3):
@@ -206,6 +222,176 @@ def cpu_baseline(T: int, pos0: int, layers: int, target_s: float = 12.0, max_lay
                       % (done, layers, T, T, pos0, t_total, layers)}
 
 
+class Timer:
+    """HIP events on torch's current stream, which every bound call uses."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def pair(self):
+        E = self.torch.cuda.Event
+        return E(enable_timing=True), E(enable_timing=True)
+
+
+def measure(workload: str, args, dev, flush) -> dict:
+    """Runs one prompt or split workload through the three timed regions."""
+    import numpy as np
+    import torch
+
+    import qsa_synth
+    import quantized_sparse_flash_amd as qsa
+
+    wl = WORKLOADS[workload]
+    T, pos0, L, kind = wl["T"], wl["pos0"], wl["layers"], wl["kind"]
+    log("bench: generating %d layer(s) of inputs (%s)" % (L, workload))
+    layers = []
+    for layer in range(L):
+        inp = qsa_synth.layer_inputs(T, pos0, layer=layer)
+        d = {k: torch.from_numpy(np.ascontiguousarray(getattr(inp, k))).to(dev)
+             for k in ("q", "kq", "ksc", "vq", "vsc")}
+        s = qsa.QsaShape(T=T, pos0=pos0, n_groups=2, budget=inp.budget, n_cells=inp.n_cells)
+        d["shape"] = s
+        d["scores"] = None if inp.scores is None else torch.from_numpy(inp.scores).to(dev)
+        d["ids"] = None
+        if inp.scores is not None:
+            d["ids"] = torch.empty((T, 2, inp.budget), dtype=torch.int32, device=dev)
+        d["out"] = torch.empty((T, s.n_heads, 256), dtype=torch.float16, device=dev)
+        need = qsa.qsa_flash_workspace_bytes(s)
+        # a workspace of its own per layer (the attend-only region prepares
+        # every layer before the attention launches run)
+        d["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        d["part"] = None
+        if kind == "split":
+            d["part"] = torch.empty((T, s.n_part_chunks, s.n_heads, qsa.PART_STRIDE),
+                                    dtype=torch.float32, device=dev)
+        d["topk"] = (qsa.bind_qsa_topk(s, d["scores"], d["ids"]) if d["scores"] is not None
+                     else None)
+        d["flash"] = qsa.bind_qsa_flash(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"],
+                                        d["ids"], None if kind == "split" else d["out"],
+                                        d["part"], d["ws"])
+        d["merge"] = qsa.bind_qsa_merge(s, d["part"], d["out"]) if kind == "split" else None
+        layers.append(d)
+    torch.cuda.synchronize()
+    budget = layers[0]["shape"].budget
+
+    def step():
+        for d in layers:
+            if d["topk"] is not None:
+                d["topk"]()
+            d["flash"]()
+            if d["merge"] is not None:
+                d["merge"]()
+
+    n_warm, steps = run_warmup(args, step, torch.cuda.synchronize)
+
+    # 1. value and ms_per_step: K steps with nothing else on the stream
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # 2. the pages' protocol: single steps after a cache flush, median + min
+    tm = Timer(torch)
+    samp = []
+    for k in range(SAMPLES):
+        flush.fill_(k & 0xFF)
+        e0, e1 = tm.pair()
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        samp.append(e0.elapsed_time(e1))
+    med, mn = statistics.median(samp), min(samp)
+
+    # 3. kernel timing: every step's qsa_flash calls back to back
+    repeat = DECODE_REPEAT if T <= 8 else 1
+    ev = [tm.pair() for _ in range(steps)]
+    for k in range(steps):
+        for d in layers:
+            if d["topk"] is not None:
+                d["topk"]()
+        ev[k][0].record()
+        for _ in range(repeat):
+            for d in layers:
+                d["flash"]()
+        ev[k][1].record()
+        for d in layers:
+            if d["merge"] is not None:
+                d["merge"]()
+    torch.cuda.synchronize()
+    call_s = sum(a.elapsed_time(b) for a, b in ev) / (steps * repeat * L) / 1e3
+    attend_s = None
+    if kind == "prompt":
+        # the attention kernel alone: every layer prepared into its own
+        # workspace first, then the attend launches back to back
+        ev = [tm.pair() for _ in range(steps)]
+        for k in range(steps):
+            for d in layers:
+                if d["topk"] is not None:
+                    d["topk"]()
+                qsa.qsa_flash_prepare(d["shape"], d["kq"], d["ksc"], d["vq"], d["vsc"],
+                                      workspace=d["ws"])
+            ev[k][0].record()
+            for d in layers:
+                qsa.qsa_flash_attend(d["shape"], d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"],
+                                     d["ids"], d["out"], workspace=d["ws"])
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        attend_s = sum(a.elapsed_time(b) for a, b in ev) / (steps * L) / 1e3
+
+    visits, by, flops = algorithmic(T, pos0, budget)
+    ms_per_step = elapsed / steps * 1e3
+    res = {"workload": workload, "T": T, "pos0": pos0, "layers": L, "kind": kind,
+           "steps": steps, "warmup": n_warm, "ms_per_step": ms_per_step,
+           "value": T * steps / elapsed, "budget": budget,
+           "samples": {"n": SAMPLES, "median_ms": med, "min_ms": mn,
+                       "tokens_per_s_at_median": T / (med / 1e3),
+                       "flush_bytes_before_each": FLUSH_BYTES,
+                       "what": "one step between HIP events, after a %d MiB write that flushes "
+                               "the Infinity Cache and the L2s" % (FLUSH_BYTES >> 20)},
+           "visits": visits, "bytes": by, "flops": flops, "call_s": call_s,
+           "attend_s": attend_s}
+    log("bench: %s %.3f ms/step, samples median %.3f / min %.3f ms, qsa_flash call %.1f us%s"
+        % (workload, ms_per_step, med, mn, call_s * 1e6,
+           "" if attend_s is None else ", attend kernel %.1f us" % (attend_s * 1e6)))
+    del layers
+    return res
+
+
+def roofline_of(r: dict, traffic) -> dict:
+    """The roofline object of a measured workload (see the module text)."""
+    T, pos0, kind = r["T"], r["pos0"], r["kind"]
+    tflops = r["flops"] / r["call_s"] / 1e12
+    identity = pos0 + T <= r["budget"]
+    if kind == "split":
+        kern = "qsa_flash in split mode: flash_rows_kernel<true>"
+    elif identity:
+        kern = "qsa_flash: dequant_chunks_kernel + flash_tile_kernel<%d>" % (
+            8 if 2 * -(-T // 10) >= 256 else 4)
+    else:
+        kern = "qsa_flash: flash_rows_kernel<false>"
+    roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
+            "traffic": traffic, "kernel": kern, "flops_per_launch": r["flops"],
+            "mean_launch_us": r["call_s"] * 1e6,
+            "launch_timing": "HIP events on the launch stream around every step's qsa_flash "
+                             "calls run back to back (the whole call: each kernel it "
+                             "enqueues%s), over a timed region of its own"
+                             % ("; decode: the split call %d times" % DECODE_REPEAT
+                                if T <= 8 else "")}
+    if traffic is not None:
+        roof["traffic_gbs"] = traffic / r["call_s"] / 1e9
+        roof["traffic_frac_of_hbm"] = roof["traffic_gbs"] / HBM_PEAK_GBS
+    if not identity:
+        # rows above budget gather their own cells: mostly from L2 and the
+        # Infinity Cache (the gathered bytes exceed what HBM could deliver)
+        roof["note"] = ("row gather: neither roofline binds; the gather latency from L2 and "
+                        "the Infinity Cache does (see gathered and traffic)")
+    return roof
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -218,6 +404,8 @@ def main():
                          "which lets the GPU clock settle)" % AUTO_WARMUP_S)
     ap.add_argument("--workload", default="t1984_pos0_x12", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-prompts", action="store_true",
+                    help="on the default workload, skip the T=512 / T=1024 figures")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device copy of this many MiB before timing (a known-size "
                          "kernel for scaling FETCH_SIZE/WRITE_SIZE counters)")
@@ -227,14 +415,10 @@ def main():
               "MI355X (--gpus %d not supported)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import qsa_synth
     import quantized_sparse_flash_amd as qsa
 
-    wl = WORKLOADS[args.workload]
-    T, pos0, L, kind = wl["T"], wl["pos0"], wl["layers"], wl["kind"]
     qsa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -246,156 +430,30 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("bench: calibration copy of %d MiB done" % args.calib_copy_mb)
-    if kind == "quantize":
-        bench_quantize(args, pos0 + T, dev)
+    if WORKLOADS[args.workload]["kind"] == "quantize":
+        bench_quantize(args, WORKLOADS[args.workload], dev)
         return
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
-    log("bench: generating %d layer(s) of inputs (%s)" % (L, args.workload))
-    layers = []
-    for layer in range(L):
-        inp = qsa_synth.layer_inputs(T, pos0, layer=layer)
-        d = {k: torch.from_numpy(np.ascontiguousarray(getattr(inp, k))).to(dev)
-             for k in ("q", "kq", "ksc", "vq", "vsc")}
-        s = qsa.QsaShape(T=T, pos0=pos0, n_groups=2, budget=inp.budget, n_cells=inp.n_cells)
-        d["scores"] = None if inp.scores is None else torch.from_numpy(inp.scores).to(dev)
-        d["ids"] = None
-        if inp.scores is not None:
-            d["ids"] = torch.empty((T, 2, inp.budget), dtype=torch.int32, device=dev)
-        d["out"] = torch.empty((T, s.n_heads, 256), dtype=torch.float16, device=dev)
-        if kind == "split":
-            d["part"] = torch.empty((T, s.n_part_chunks, s.n_heads, qsa.PART_STRIDE),
-                                    dtype=torch.float32, device=dev)
-        d["shape"] = s
-        # a workspace of its own per layer (the kernel-timing region
-        # prepares every layer before the attend launches run)
-        need = qsa.qsa_flash_workspace_bytes(s)
-        d["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
-        layers.append(d)
-    # one workspace serves every layer: the calls run in order on one stream
-    ws = max((d["ws"] for d in layers if d["ws"] is not None), key=lambda t: t.numel(),
-             default=None)
-    torch.cuda.synchronize()
-    budget = layers[0]["shape"].budget
-
-    def step():
-        for d in layers:
-            s = d["shape"]
-            if d["scores"] is not None:
-                qsa.qsa_topk(s, d["scores"], d["ids"])
-            if kind == "split":
-                qsa.qsa_flash(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"], None,
-                              d["part"])
-                qsa.qsa_merge(s, d["part"], d["out"])
-            else:
-                qsa.qsa_flash_prepare(s, d["kq"], d["ksc"], d["vq"], d["vsc"], workspace=ws)
-                qsa.qsa_flash_attend(s, d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"], d["ids"],
-                                     d["out"], workspace=ws)
-
-    repeat = DECODE_REPEAT if T <= 8 else 1
-
-    def step_timed(ev0, ev1) -> int:
-        """The same step with its dominant launches back to back between two
-        events: every layer is prepared (into its own workspace) before the
-        attend launches run; a decode step's split qsa_flash call, which
-        only rewrites its partials, runs DECODE_REPEAT times (once for
-        prompt-sized splits).  Returns the number of launches between the
-        events."""
-        if kind == "split":
-            for d in layers:
-                if d["scores"] is not None:
-                    qsa.qsa_topk(d["shape"], d["scores"], d["ids"])
-            ev0.record()
-            for _ in range(repeat):
-                for d in layers:
-                    qsa.qsa_flash(d["shape"], d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"],
-                                  d["ids"], None, d["part"])
-            ev1.record()
-            for d in layers:
-                qsa.qsa_merge(d["shape"], d["part"], d["out"])
-            return repeat * L
-        for d in layers:
-            s = d["shape"]
-            if d["scores"] is not None:
-                qsa.qsa_topk(s, d["scores"], d["ids"])
-            qsa.qsa_flash_prepare(s, d["kq"], d["ksc"], d["vq"], d["vsc"], workspace=d["ws"])
-        ev0.record()
-        for d in layers:
-            qsa.qsa_flash_attend(d["shape"], d["q"], d["kq"], d["ksc"], d["vq"], d["vsc"],
-                                 d["ids"], d["out"], workspace=d["ws"])
-        ev1.record()
-        return L
-
-    run_warmup(args, step, torch.cuda.synchronize)
-
-    # timed region 1 (value, ms_per_step): K steps with nothing else on the
-    # stream.  An event between two kernels costs the stream a few
-    # microseconds and reads the next kernel's dispatch as part of its time,
-    # so the launch durations come from a second region.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    # timed region 2 (roofline): K more steps, HIP events on the launch
-    # stream (torch's current stream) around each step's dominant launches
-    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-          for _ in range(args.steps)]
-    n_launch = 0
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for k in range(args.steps):
-        n_launch += step_timed(*ev[k])
-    torch.cuda.synchronize()
-    elapsed_ev = time.perf_counter() - t1
-    mean_launch_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) / n_launch / 1e3
-
-    ms_per_step = elapsed / args.steps * 1e3
-    value = T * args.steps / elapsed
-    visits, by, flops = algorithmic(T, pos0, budget)
-    gbs = by / mean_launch_s / 1e9
-    tflops = flops / mean_launch_s / 1e12
-    log("bench: %.3f ms/step (%.3f in the kernel-timing region), attention kernel mean %.1f us, "
-        "%.0f GB/s algorithmic, %.1f TFLOP/s"
-        % (ms_per_step, elapsed_ev / args.steps * 1e3, mean_launch_s * 1e6, gbs, tflops))
-
-    traffic = measured_traffic(args.workload)
-    identity_tile = pos0 + T <= budget and kind == "prompt"
-    if identity_tile:
-        roofline = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
-                    "traffic": traffic,
-                    # the library takes 8-wave workgroups of 10 tokens when at
-                    # least 256 of them cover the prompt, else 4-wave ones of 5
-                    "kernel": "flash_tile_kernel<%d> (qsa_flash_attend)"
-                              % (8 if 2 * -(-T // 10) >= 256 else 4),
-                    "flops_per_launch": flops, "mean_launch_us": mean_launch_s * 1e6,
-                    "launch_timing": LAUNCH_TIMING}
-    else:
-        roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                    "kernel": ("flash_rows_kernel<true> (split qsa_flash)" if kind == "split"
-                               else "flash_rows_kernel<false> (qsa_flash_attend)"),
-                    "algorithmic_bytes_per_launch": by, "mean_launch_us": mean_launch_s * 1e6,
-                    "launch_timing": LAUNCH_TIMING}
-        if kind == "split":
-            # the (o, m, l) records the split call writes (and the merge
-            # reads): one per (token, selected 64-cell chunk, head)
-            n_rec = sum(-(-min(pos0 + t + 1, budget) // 64) for t in range(T)) * 2 * 12
-            roofline["partial_bytes_per_launch"] = n_rec * qsa.PART_STRIDE * 4
+    r = measure(args.workload, args, dev, flush)
+    T, pos0, L, kind = r["T"], r["pos0"], r["layers"], r["kind"]
+    call_s = r["call_s"]
+    gbs = r["bytes"] / call_s / 1e9
+    roof = roofline_of(r, measured_traffic(args.workload))
     m5 = PAGES_M5_TOKS.get(T) if (pos0 == 0 and L == 12) else None
     steps_desc = {"prompt": "qsa_flash", "split": "qsa_topk + split qsa_flash + qsa_merge"}
+    budget = r["budget"]
     line = {
         "metric": "qsa_flash query-tokens/s at T=%d (%d layer%s)" % (T, L, "s" if L > 1 else ""),
-        "value": value,
+        "value": r["value"],
         "unit": "query-tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "steps": r["steps"],
+        "warmup": r["warmup"],
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": (value / m5) if m5 else None,
+        "vs_baseline": (r["value"] / m5) if m5 else None,
         "dtype": "f16",
         "precision": "int8 K/V codes with fp16 scales, dequantised to fp16; fp16 Q, P and out; "
                      "fp16 MFMA with fp32 accumulation",
@@ -408,32 +466,53 @@ def main():
                                   else "", steps_desc[kind], budget),
                    "T": T, "pos0": pos0, "layers": L, "n_groups": 2, "heads_per_group": 12,
                    "head_dim": 256, "budget": budget},
-        "roofline": roofline,
+        "samples": r["samples"],
+        "roofline": roof,
         "gathered": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": by,
-                     "cell_visits_per_launch": visits},
-        "mfma": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
-                 "flops_per_launch": flops},
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": r["bytes"],
+                     "cell_visits_per_launch": r["visits"]},
     }
+    if r["attend_s"] is not None:
+        at = r["flops"] / r["attend_s"] / 1e12
+        line["attend_only"] = {
+            "bound": "mfma", "achieved": at, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": at / MFMA_F16_PEAK_TFLOPS, "mean_launch_us": r["attend_s"] * 1e6,
+            "kernel": "the attention kernel of qsa_flash_attend (tile or rows kernel)",
+            "launch_timing": "HIP events around every step's attend launches run back to "
+                             "back, every layer prepared into its own workspace first"}
     if m5:
         line["vs_baseline_note"] = ("value / the pages' Apple M5 figure (%.0f query-tokens/s, "
                                     "12 layers at T=%d); another machine, context only" % (m5, T))
+    if args.workload == "t1984_pos0_x12" and not args.no_other_prompts:
+        other = {}
+        for wl in OTHER_PROMPTS:
+            o = measure(wl, argparse.Namespace(steps=None, warmup=None), dev, flush)
+            ro = roofline_of(o, None)
+            other[wl] = {"value": o["value"], "unit": "query-tokens/s",
+                         "ms_per_step": o["ms_per_step"], "samples": o["samples"],
+                         "qsa_flash_call_us": o["call_s"] * 1e6,
+                         "attend_kernel_us": o["attend_s"] * 1e6,
+                         "mfma_frac": ro["frac"], "steps": o["steps"]}
+        line["other_prompts"] = other
+    del flush
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle (bounded sample)")
-        line["cpu_baseline"] = cpu_baseline(T, pos0, L)
+        cb = cpu_baseline(T, pos0, L)
+        if T == 1984 and pos0 == 0:
+            cb["single_thread_t512"] = single_thread_oracle_t512()
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 
-def bench_quantize(args, n_cells: int, dev) -> None:
+def bench_quantize(args, wl, dev) -> None:
     """qsa_quantize on the fp16 K and V rows of a 2-group cache of n_cells
     cells; one step quantises both tensors (two calls)."""
-    import numpy as np
     import torch
 
     import qsa_synth
     import quantized_sparse_flash_amd as qsa
 
+    n_cells = wl["pos0"] + wl["T"]
     G = 2
     rows = G * n_cells
     log("bench: generating fp16 K/V rows (%d cells x %d groups)" % (n_cells, G))
@@ -446,37 +525,37 @@ def bench_quantize(args, n_cells: int, dev) -> None:
         for i in range(2):
             qsa.qsa_quantize(xs[i], codes[i], scales[i])
 
-    run_warmup(args, step, torch.cuda.synchronize)
+    n_warm, steps = run_warmup(args, step, torch.cuda.synchronize)
     # value from K plain steps; launch durations from K more steps, each
     # repeated QUANT_REPEAT times between two events
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-          for _ in range(args.steps)]
-    for k in range(args.steps):
+    tm = Timer(torch)
+    ev = [tm.pair() for _ in range(steps)]
+    for k in range(steps):
         ev[k][0].record()
         for _ in range(QUANT_REPEAT):
             step()
         ev[k][1].record()
     torch.cuda.synchronize()
     mean_launch_s = (sum(e0.elapsed_time(e1) for e0, e1 in ev)
-                     / (2 * QUANT_REPEAT * args.steps) / 1e3)
+                     / (2 * QUANT_REPEAT * steps) / 1e3)
     by = rows * QUANT_ROW_BYTES
     gbs = by / mean_launch_s / 1e9
-    value = rows * args.steps / elapsed
+    value = rows * steps / elapsed
     log("bench: %.3f ms/step, quantize kernel mean %.1f us, %.0f GB/s"
-        % (elapsed / args.steps * 1e3, mean_launch_s * 1e6, gbs))
+        % (elapsed / steps * 1e3, mean_launch_s * 1e6, gbs))
     line = {
         "metric": "qsa_quantize cells/s (K and V rows of 2 groups)",
         "value": value,
         "unit": "cells/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": elapsed / args.steps * 1e3,
+        "steps": steps,
+        "warmup": n_warm,
+        "ms_per_step": elapsed / steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -484,14 +563,17 @@ def bench_quantize(args, n_cells: int, dev) -> None:
         "precision": "fp16 rows in, int8 codes + fp16 scales out; divisions and rounding "
                      "decisions in IEEE fp32",
         "data": "synthetic (seeded: fp16 N(0,1) x 10^U(-3,1) per 64-dim block)",
-        "config": {"workload": "%s: qsa_quantize of K and V, 2 groups x %d cells x 256 dims"
-                               % (args.workload, n_cells),
+        "config": {"workload": "quantize_kv_31984: qsa_quantize of K and V, 2 groups x %d "
+                               "cells x 256 dims" % n_cells,
                    "n_cells": n_cells, "n_groups": G, "head_dim": 256},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("quantize_kv_31984"),
                      "kernel": "quantize_kernel (qsa_quantize)",
                      "algorithmic_bytes_per_launch": by, "mean_launch_us": mean_launch_s * 1e6,
-                     "launch_timing": LAUNCH_TIMING},
+                     "launch_timing": "HIP events around %d back-to-back K+V quantiser call "
+                                      "pairs per step, over a timed region of its own"
+                                      % QUANT_REPEAT},
     }
     if not args.no_cpu_baseline:
         import oracle

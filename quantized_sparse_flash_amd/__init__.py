@@ -287,3 +287,67 @@ def qsa_quantize(x, codes, scales, stream=None) -> None:
     rc = load_library().qsa_quantize(rows, HEAD_DIM, xp, cp, sp, _stream(stream))
     if rc != QSA_OK:
         raise QsaError(rc, "qsa_quantize")
+
+
+class BoundCall:
+    """One C-ABI call with its arguments marshalled and checked once: calling
+    the object enqueues the call again on the stream it was bound to.  For
+    loops that issue the same launch many times (12 layers per step); the
+    tensors must stay alive and in place while the object is used."""
+
+    def __init__(self, fn, name, args, keep):
+        self._fn, self._name, self._args, self._keep = fn, name, args, keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != QSA_OK:
+            raise QsaError(rc, self._name)
+
+
+def bind_qsa_flash(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None, workspace=None,
+                   stream=None) -> BoundCall:
+    """qsa_flash with the arguments of ``qsa_flash`` (checked here, once)."""
+    import torch
+    s = shape
+    if part is None and workspace is None:
+        workspace = flash_workspace(s, q.device)
+    H, D, N, G = s.n_heads, s.head_dim, s.n_cells, s.n_groups
+    cs = s.c()
+    args = [ctypes.byref(cs),
+            _dev_ptr(q, "q", torch.float16, (s.T, H, D)),
+            _dev_ptr(kq, "kq", torch.int8, (G, N, D)),
+            _dev_ptr(ksc, "ksc", torch.float16, (G, N, D // 64)),
+            _dev_ptr(vq, "vq", torch.int8, (G, N, D)),
+            _dev_ptr(vsc, "vsc", torch.float16, (G, N, D // 64)),
+            _dev_ptr(ids, "ids", torch.int32, (s.T, G, s.budget)),
+            _dev_ptr(out, "out", torch.float16, (s.T, H, D)),
+            _dev_ptr(part, "part", torch.float32, (s.T, s.n_part_chunks, H, PART_STRIDE)),
+            None if workspace is None else _dev_ptr(workspace, "workspace", torch.uint8),
+            ctypes.c_int64(0 if workspace is None else workspace.numel()),
+            _stream(stream)]
+    return BoundCall(load_library().qsa_flash, "qsa_flash", args,
+                     (cs, q, kq, ksc, vq, vsc, ids, out, part, workspace))
+
+
+def bind_qsa_topk(shape: QsaShape, scores, ids, stream=None) -> BoundCall:
+    """qsa_topk with the arguments of ``qsa_topk`` (checked here, once)."""
+    import torch
+    s = shape
+    cs = s.c()
+    args = [ctypes.byref(cs),
+            _dev_ptr(scores, "scores", torch.float32, (s.T, s.n_groups, s.n_cells)),
+            _dev_ptr(ids, "ids", torch.int32, (s.T, s.n_groups, s.budget)),
+            _stream(stream)]
+    return BoundCall(load_library().qsa_topk, "qsa_topk", args, (cs, scores, ids))
+
+
+def bind_qsa_merge(shape: QsaShape, part, out, stream=None) -> BoundCall:
+    """qsa_merge with the arguments of ``qsa_merge`` (checked here, once)."""
+    import torch
+    s = shape
+    cs = s.c()
+    args = [ctypes.byref(cs),
+            _dev_ptr(part, "part", torch.float32, (s.T, s.n_part_chunks, s.n_heads, PART_STRIDE)),
+            _dev_ptr(out, "out", torch.float16, (s.T, s.n_heads, s.head_dim)),
+            _stream(stream)]
+    return BoundCall(load_library().qsa_merge, "qsa_merge", args, (cs, part, out))

@@ -159,3 +159,15 @@ def test_quantize_arguments_are_validated():
     assert q(4, 256, A, A + 4, A) == qsa.QSA_ERR_ARG              # codes 16 B
     assert q(4, 256, A, A, A + 1) == qsa.QSA_ERR_ARG              # scales 2 B
     assert q(4, 256, A, A, 0) == qsa.QSA_ERR_ARG
+
+
+def test_page_case_lists_hold_the_pages_counts():
+    # the GPU parity tests take their cases from these lists: the r9 result's
+    # 13 byte-checked cases, the r14 16-case grid, the r27 40-case matrix
+    g = json.load(open(GOLDEN))
+    assert len(g["cases_r9_bitwise"]["value"]) == 13
+    grid = g["cases_r14_grid"]["value"]
+    assert len(grid["T"]) * len(grid["pos0"]) == 16
+    dm = g["cases_r27_decode"]["value"]
+    assert len(dm["pos"]) * len(dm["tokens"]) == 40
+
