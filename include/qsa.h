@@ -47,6 +47,8 @@ extern "C" {
 #define QSA_ERR_UNSUPPORTED (-2) /* heads_per_group != 12, head_dim != 256, budget too large */
 #define QSA_ERR_SHAPE (-3)       /* T < 1, pos0 < 0, n_groups < 1, n_cells < pos0 + T, ... */
 #define QSA_ERR_LAUNCH (-4)      /* the HIP runtime rejected a kernel launch */
+#define QSA_ERR_TOO_LARGE (-5)   /* qsa_flash_noalloc: the shape needs more scratch than it holds */
+#define QSA_ERR_DEVICE (-6)      /* qsa_flash_noalloc: the current HIP device could not be queried */
 
 /* Library limits. */
 #define QSA_HEADS_PER_GROUP 12 /* query heads that share one KV group */
@@ -56,6 +58,7 @@ extern "C" {
 #define QSA_PART_STRIDE 258    /* floats per partial record: o[256], m, l */
 #define QSA_MAX_BUDGET 65536   /* largest supported budget */
 #define QSA_DEFAULT_BUDGET 2051
+#define QSA_NOALLOC_SCRATCH_BYTES (16 << 20) /* device scratch held by qsa_flash_noalloc */
 
 /* Shape of one prompt chunk of one layer. */
 typedef struct {
@@ -155,6 +158,29 @@ int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq
  * 64-cell chunk (fp16 K and V^T).
  */
 int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
+
+/*
+ * qsa_flash_noalloc -- qsa_flash for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, layouts,
+ * results and errors as qsa_flash without the workspace: the fused path's
+ * scratch is instead a static device array of QSA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that each GPU the library runs on holds until the process ends;
+ * its address is resolved (hipGetSymbolAddress) on the first call on each
+ * device, with that device current.  The call itself allocates nothing.
+ * Every call on one GPU shares that GPU's array, so two calls that overlap
+ * in time on the same GPU (other streams, other threads) race and give
+ * unspecified output; calls ordered on one stream are fine.  Nothing in the
+ * array needs to start at zero (each call writes every byte it reads).
+ *   returns QSA_ERR_TOO_LARGE when qsa_flash_workspace_bytes(shape) exceeds
+ *   QSA_NOALLOC_SCRATCH_BYTES (e.g. more than 256 KV-group x 64-cell
+ *   chunks of identity prefix: 2 groups up to budget 8192), checked before
+ *   anything else touches the device; QSA_ERR_DEVICE when the device or
+ *   the array's address cannot be queried.
+ */
+int qsa_flash_noalloc(const qsa_shape *shape, const _Float16 *q, const int8_t *kq,
+                      const _Float16 *ksc, const int8_t *vq, const _Float16 *vsc,
+                      const int32_t *ids, _Float16 *out, float *part, void *stream);
 
 /*
  * qsa_merge -- log-sum-exp merge of split-mode partials (page "round 27

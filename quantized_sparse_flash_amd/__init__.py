@@ -12,6 +12,8 @@ Entry points (all asynchronous on the current stream):
   qsa_flash(shape, q, kq, ksc, vq, vsc, ids, out, part=None)   attention
   qsa_flash_prepare(shape, kq, ksc, vq, vsc, workspace)         fused mode, first half
   qsa_flash_attend(shape, q, kq, ksc, vq, vsc, ids, out, workspace)   ... second half
+  qsa_flash_noalloc(shape, q, kq, ksc, vq, vsc, ids, out, part=None)
+                                                    qsa_flash with library-held scratch
   qsa_merge(shape, part, out)                                  LSE merge
   qsa_quantize(x, codes, scales)                               K/V quantiser
 """
@@ -30,6 +32,9 @@ QSA_ERR_ARG = -1
 QSA_ERR_UNSUPPORTED = -2
 QSA_ERR_SHAPE = -3
 QSA_ERR_LAUNCH = -4
+QSA_ERR_TOO_LARGE = -5
+QSA_ERR_DEVICE = -6
+NOALLOC_SCRATCH_BYTES = 16 << 20
 HEADS_PER_GROUP = 12
 HEAD_DIM = 256
 CHUNK = 64
@@ -38,7 +43,8 @@ DEFAULT_BUDGET = 2051
 MAX_BUDGET = 65536
 
 EXPORTED = ("qsa_topk", "qsa_flash", "qsa_flash_prepare", "qsa_flash_attend", "qsa_merge",
-            "qsa_quantize", "qsa_status_string", "qsa_part_elems", "qsa_flash_workspace_bytes")
+            "qsa_quantize", "qsa_status_string", "qsa_part_elems", "qsa_flash_workspace_bytes",
+            "qsa_flash_noalloc")
 
 
 class QsaError(RuntimeError):
@@ -101,6 +107,7 @@ def load_library(path: str = LIB_PATH):
     lib.qsa_flash.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]
     lib.qsa_flash_prepare.argtypes = [SP, P, P, P, P, P, ctypes.c_int64, P]
     lib.qsa_flash_attend.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_int64, P]
+    lib.qsa_flash_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     lib.qsa_flash_workspace_bytes.argtypes = [SP]
     lib.qsa_flash_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_merge.argtypes = [SP, P, P, P]
@@ -110,7 +117,7 @@ def load_library(path: str = LIB_PATH):
     lib.qsa_part_elems.argtypes = [SP]
     lib.qsa_part_elems.restype = ctypes.c_int64
     for f in (lib.qsa_topk, lib.qsa_flash, lib.qsa_flash_prepare, lib.qsa_flash_attend,
-              lib.qsa_merge, lib.qsa_quantize):
+              lib.qsa_merge, lib.qsa_quantize, lib.qsa_flash_noalloc):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -212,6 +219,29 @@ def qsa_flash(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None, workspa
     rc = load_library().qsa_flash(ctypes.byref(cs), *args, ws_ptr, ws_bytes, _stream(stream))
     if rc != QSA_OK:
         raise QsaError(rc, "qsa_flash")
+
+
+def qsa_flash_noalloc(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None,
+                      stream=None) -> None:
+    """qsa_flash without a workspace: the library's own static device scratch
+    (NOALLOC_SCRATCH_BYTES per GPU) serves the fused path; calls that overlap
+    in time on one GPU race.  Raises QsaError (QSA_ERR_TOO_LARGE) for shapes
+    whose workspace would exceed that scratch."""
+    import torch
+    s = shape
+    H, D, N, G = s.n_heads, s.head_dim, s.n_cells, s.n_groups
+    args = [_dev_ptr(q, "q", torch.float16, (s.T, H, D)),
+            _dev_ptr(kq, "kq", torch.int8, (G, N, D)),
+            _dev_ptr(ksc, "ksc", torch.float16, (G, N, D // 64)),
+            _dev_ptr(vq, "vq", torch.int8, (G, N, D)),
+            _dev_ptr(vsc, "vsc", torch.float16, (G, N, D // 64)),
+            _dev_ptr(ids, "ids", torch.int32, (s.T, G, s.budget)),
+            _dev_ptr(out, "out", torch.float16, (s.T, H, D)),
+            _dev_ptr(part, "part", torch.float32, (s.T, s.n_part_chunks, H, PART_STRIDE))]
+    cs = s.c()
+    rc = load_library().qsa_flash_noalloc(ctypes.byref(cs), *args, _stream(stream))
+    if rc != QSA_OK:
+        raise QsaError(rc, "qsa_flash_noalloc")
 
 
 def _kv_args(s: QsaShape, kq, ksc, vq, vsc) -> list:

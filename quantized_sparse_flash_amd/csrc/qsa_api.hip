@@ -6,8 +6,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qsa.h"
 #include "qsa_launch.h"
+
+// Device scratch of qsa_flash_noalloc: one copy per GPU, alive until the
+// process ends.  In host code `scratch` is only a stand-in for the symbol:
+// its device address comes from hipGetSymbolAddress (see scratch_ptr).
+static __device__ __align__(256) uint8_t scratch[QSA_NOALLOC_SCRATCH_BYTES];
 
 
 namespace {
@@ -52,6 +59,9 @@ const char* qsa_status_string(int status) {
     case QSA_ERR_UNSUPPORTED: return "unsupported configuration (heads_per_group, head_dim or budget)";
     case QSA_ERR_SHAPE: return "invalid shape (T, pos0, n_groups or n_cells)";
     case QSA_ERR_LAUNCH: return "kernel launch failed";
+    case QSA_ERR_TOO_LARGE:
+      return "shape needs more scratch than qsa_flash_noalloc holds (QSA_NOALLOC_SCRATCH_BYTES)";
+    case QSA_ERR_DEVICE: return "HIP device query failed";
     default: return "unknown status";
   }
 }
@@ -193,6 +203,58 @@ int qsa_quantize(int64_t n_rows, int32_t dim, const _Float16* x, int8_t* codes,
   if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2))
     return QSA_ERR_ARG;
   return launch_status(qsa::launch_quantize(x, codes, scales, n_rows, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device, once resolved
+
+// Device address of the current device's copy of `scratch`, resolved on the
+// first call on that device (with it current) and kept; nullptr on failure.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_flash_noalloc(const qsa_shape* s, const _Float16* q, const int8_t* kq,
+                      const _Float16* ksc, const int8_t* vq, const _Float16* vsc,
+                      const int32_t* ids, _Float16* out, float* part, void* stream) {
+  // every host-side check of qsa_flash first (nothing touches the device)
+  qsa::RowArgs a;
+  int rc = flash_args(s, q, kq, ksc, vq, vsc, ids, out, part, &a);
+  if (rc != QSA_OK) return rc;
+  if (part) {
+    if (!q || !aligned(q, 16) || !aligned(part, 16)) return QSA_ERR_ARG;
+    if (any_above_budget(s) && (!ids || !aligned(ids, 4))) return QSA_ERR_ARG;
+  } else {
+    rc = check_attend(s, q, ids, out);
+    if (rc != QSA_OK) return rc;
+  }
+  const int64_t need =
+      part ? 0 : qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+  if (need > QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_ptr();
+    if (!ws) return QSA_ERR_DEVICE;
+  }
+  return qsa_flash(s, q, kq, ksc, vq, vsc, ids, out, part, ws,
+                   need > 0 ? (int64_t)QSA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 }  // extern "C"

@@ -171,3 +171,28 @@ def test_page_case_lists_hold_the_pages_counts():
     dm = g["cases_r27_decode"]["value"]
     assert len(dm["pos"]) * len(dm["tokens"]) == 40
 
+
+def test_noalloc_checks_arguments_and_scratch_size_on_the_host():
+    # qsa_flash_noalloc: q, kq, ksc, vq, vsc, ids, out, part.  Every check
+    # below fails before the device is touched (this machine may have none)
+    lib = qsa.load_library()
+    A = 0x10000
+    E = qsa.QSA_ERR_ARG
+    under = qsa.QsaShape(T=8, pos0=0)
+    over = qsa.QsaShape(T=8, pos0=2050)
+    assert _raw(lib, "qsa_flash_noalloc", under, 0, A, A, A, A, 0, A, 0, None) == E   # q
+    assert _raw(lib, "qsa_flash_noalloc", under, A, A, A, A, A, 0, 0, 0, None) == E   # out
+    assert _raw(lib, "qsa_flash_noalloc", over, A, A, A, A, A, 0, A, 0, None) == E    # ids
+    assert _raw(lib, "qsa_flash_noalloc", under, A, A, A + 4, A, A, 0, A, 0, None) == E
+    assert _raw(lib, "qsa_flash_noalloc", qsa.QsaShape(T=0, pos0=0), A, A, A, A, A, 0, A, 0,
+                None) == qsa.QSA_ERR_SHAPE
+    # 4 groups x 1024 chunks of identity prefix need 256 MiB of images
+    big = qsa.QsaShape(T=1, pos0=65535, n_groups=4, budget=65536)
+    assert qsa.qsa_flash_workspace_bytes(big) > qsa.NOALLOC_SCRATCH_BYTES
+    assert _raw(lib, "qsa_flash_noalloc", big, A, A, A, A, A, 0, A, 0, None) == \
+        qsa.QSA_ERR_TOO_LARGE
+    # 2 groups up to an 8192-cell prefix fit exactly
+    fit = qsa.QsaShape(T=1, pos0=8191, n_groups=2, budget=8192)
+    assert qsa.qsa_flash_workspace_bytes(fit) == qsa.NOALLOC_SCRATCH_BYTES
+    assert qsa.qsa_status_string(qsa.QSA_ERR_TOO_LARGE) != "unknown status"
+    assert qsa.qsa_status_string(qsa.QSA_ERR_DEVICE) != "unknown status"
