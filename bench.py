@@ -368,8 +368,10 @@ def roofline_of(r: dict, traffic) -> dict:
     if kind == "split":
         kern = "qsa_flash in split mode: flash_rows_kernel<true>"
     elif identity:
+        # 8-wave workgroups of 128 queries when at least 256 of them cover
+        # the prompt (2 groups), else 4-wave ones of 64
         kern = "qsa_flash: dequant_chunks_kernel + flash_tile_kernel<%d>" % (
-            8 if 2 * -(-T // 10) >= 256 else 4)
+            8 if 2 * -(-T * 12 // 128) >= 256 else 4)
     else:
         kern = "qsa_flash: flash_rows_kernel<false>"
     roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,

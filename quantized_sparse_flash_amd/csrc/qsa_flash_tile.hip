@@ -1,5 +1,6 @@
 // qsa_flash_tile.hip -- fused attention for tokens under the budget, tiled
-// over 10 consecutive tokens of one KV group.
+// over 128 consecutive queries (the (token, head) pairs in order) of one KV
+// group.
 //
 // Pages: "round 6 track b - qsa flash" (delivered change: a token that sees
 // at most `budget` cells attends to all of them, ids derived in the kernel;
@@ -28,13 +29,14 @@
 //     Both swizzles make the 16-byte MFMA operand reads conflict-free for
 //     any 16 consecutive rows.  Cells past the last visible one are zero.
 //
-//   flash_tile_kernel  one workgroup per (group, 10 tokens): 120 queries
-//     (10 tokens x 12 heads) on 8 waves x 16 query slots, two waves per
-//     SIMD, so that one wave's softmax runs on the VALU while the other's
-//     products occupy the matrix core.  When that grid would not cover the
-//     256 CUs (short prompts), workgroups of 4 waves take 5 tokens each:
-//     twice the workgroups, each running its chunks about twice as fast on
-//     one wave per SIMD.  Products on v_mfma_f32_16x16x32_f16
+//   flash_tile_kernel  one workgroup per (group, block of 128 consecutive
+//     queries of the group's (token, head) pairs, about 10.7 tokens) on 8
+//     waves x 16 query slots, two waves per SIMD, so that one wave's softmax
+//     runs on the VALU while the other's products occupy the matrix core;
+//     every slot holds a query but in a group's last block.  When that grid
+//     would not cover the 256 CUs (short prompts), workgroups of 4 waves
+//     take 64 queries each: twice the workgroups, each running its chunks
+//     about twice as fast on one wave per SIMD.  Products on v_mfma_f32_16x16x32_f16
 //     with queries in the N dimension:
 //       S^T[64 cells][16 queries] = K Q^T   (A = K from LDS, B = Q^T held in
 //                                            registers for the whole block)
@@ -78,8 +80,13 @@ namespace qsa {
 namespace {
 
 constexpr int kQpw = 16;  // query slots per wave
-// Whole tokens per workgroup of `waves` waves: 10 with 8 waves, 5 with 4.
-__host__ __device__ constexpr int tile_tokens(int waves) { return kQpw * waves / kHpg; }
+// Queries per workgroup of `waves` waves: 128 with 8 waves, 64 with 4.  A
+// block takes that many consecutive queries of the group's (token, head)
+// pairs in order, so every query slot is used but in a group's last block.
+__host__ __device__ constexpr int tile_queries(int waves) { return kQpw * waves; }
+__host__ __device__ inline int tile_blocks(int t_count, int waves) {
+  return (t_count * kHpg + tile_queries(waves) - 1) / tile_queries(waves);
+}
 // MI355X compute units: below this many 8-wave workgroups the grid would
 // leave CUs idle, and 4-wave workgroups of half as many tokens are used.
 constexpr int kCus = 256;
@@ -244,19 +251,21 @@ template <int kWaves>
 __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, int t_count,
                                                                     int nchunks,
                                                                     const uint8_t* ws) {
-  constexpr int kTileTokens = tile_tokens(kWaves);
+  constexpr int kQpb = tile_queries(kWaves);
   constexpr int kCopyOps = kHalf / 1024 / kWaves;  // 1 KB copies per wave per image
   // K(c) lives in kv[c & 1], V^T(c) in kv[2 + (c & 1)]
   __shared__ __attribute__((aligned(16))) uint8_t kv[4 * kHalf];
   __shared__ int s_redo;  // set when the fast pass must be redone exactly
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.G, H = G * kHpg;
-  const int n_blocks = (t_count + kTileTokens - 1) / kTileTokens;
+  const int n_blocks = tile_blocks(t_count, kWaves);
   // longest blocks first; consecutive workgroups alternate KV groups
   const int g = blockIdx.x % G;
   const int blk = n_blocks - 1 - blockIdx.x / G;
-  const int t0 = blk * kTileTokens;
-  const int t_last = min(t0 + kTileTokens, t_count) - 1;
+  const int q0 = blk * kQpb;                                 // first query of the block
+  const int q_last = min(q0 + kQpb, t_count * kHpg) - 1;     // last one
+  const int t0 = q0 / kHpg;
+  const int t_last = q_last / kHpg;
   const int nkv_min = a.pos0 + t0 + 1;  // cells every token of the block sees
   const int nkv_max = a.pos0 + t_last + 1;
   const int nch = (nkv_max + kChunk - 1) / kChunk;
@@ -265,10 +274,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   const int n = lane & 15, j = lane >> 4;
 
   // ---- this lane's query: slot kQpw w + n of the workgroup
-  const int qs = kQpw * w + n;
-  const int qt = t0 + qs / kHpg;
+  const int qs = q0 + kQpw * w + n;
+  const bool qvalid = qs <= q_last;
+  const int qt = qs / kHpg;
   const int qh = g * kHpg + qs % kHpg;
-  const bool qvalid = qs < kTileTokens * kHpg && qt <= t_last;
   const int nkv_q = qvalid ? a.pos0 + qt + 1 : 1;
   // ---- LDS read addresses of this lane's operand fragments
   // K: row (cell) 16 mt + n, group 4 s + j; s = 4 v + u -> the XOR touches
@@ -626,13 +635,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
 #pragma unroll
       for (int r = 0; r < kQpw / 2; ++r) {
         const int qn = 2 * r + half_row;  // query slot kQpw w + qn
-        const int s2 = kQpw * w + qn;
-        const int t2 = t0 + s2 / kHpg;
+        const int s2 = q0 + kQpw * w + qn;
         const half8_t v = *reinterpret_cast<const half8_t*>(tile + qn * kRowB + 16 * seg);
-        if (s2 < kTileTokens * kHpg && t2 <= t_last)
+        if (s2 <= q_last)
           __builtin_nontemporal_store(
-              v, reinterpret_cast<half8_t*>(
-                     a.out + ((int64_t)t2 * H + g * kHpg + s2 % kHpg) * kHeadDim + 8 * seg));
+              v, reinterpret_cast<half8_t*>(a.out + ((int64_t)(s2 / kHpg) * H + g * kHpg +
+                                                     s2 % kHpg) * kHeadDim + 8 * seg));
       }
     }
     return false;
@@ -668,12 +676,12 @@ hipError_t launch_tile_attend(const RowArgs& a, int t_count, const void* ws, hip
   const int n_needed = a.pos0 + t_count;
   const int nchunks = (n_needed + kChunk - 1) / kChunk;
   const uint8_t* img = static_cast<const uint8_t*>(ws);
-  const int blocks8 = (t_count + tile_tokens(8) - 1) / tile_tokens(8);
+  const int blocks8 = tile_blocks(t_count, 8);
   if (blocks8 * a.G >= kCus) {
     flash_tile_kernel<8><<<dim3(blocks8 * a.G), dim3(8 * 64), 0, stream>>>(a, t_count, nchunks,
                                                                              img);
   } else {
-    const int blocks4 = (t_count + tile_tokens(4) - 1) / tile_tokens(4);
+    const int blocks4 = tile_blocks(t_count, 4);
     flash_tile_kernel<4><<<dim3(blocks4 * a.G), dim3(4 * 64), 0, stream>>>(a, t_count, nchunks,
                                                                              img);
   }

@@ -110,11 +110,11 @@ def test_scores_growing_after_the_first_chunk(late_scale):
     _check(gpu_flash(inp), ref)
 
 
-@pytest.mark.parametrize("T,late_scale", [(1000, None), (1000, 0.5), (1300, None), (1300, 0.5)])
+@pytest.mark.parametrize("T,late_scale", [(1000, None), (1000, 0.5), (1400, None), (1400, 0.5)])
 def test_both_tile_widths_whole_tensor(T, late_scale):
-    # prompts under budget run 8-wave workgroups of 10 tokens when that
-    # grid covers the 256 CUs (2 groups x 130 blocks at T=1300) and 4-wave
-    # workgroups of 5 tokens otherwise (T=1000); late_scale 0.5 makes later
+    # prompts under budget run 8-wave workgroups of 128 queries when that
+    # grid covers the 256 CUs (2 groups x 132 blocks at T=1400) and 4-wave
+    # workgroups of 64 queries otherwise (T=1000); late_scale 0.5 makes later
     # chunks outgrow chunk 0's reference, so the exact rescaling pass runs
     inp = qsa_synth.layer_inputs(T, 0, seed=17)
     if late_scale is not None:
@@ -215,10 +215,10 @@ def test_other_group_counts(G, T, pos0):
     _check(gpu_merge(inp, gpu_flash(inp, ids, dev, split=True)), ref)
 
 
-@pytest.mark.parametrize("G,T", [(3, 900), (4, 700), (1, 1984)])
+@pytest.mark.parametrize("G,T", [(3, 910), (4, 700), (1, 1984)])
 def test_other_group_counts_at_prompt_size(G, T):
-    # prompts long enough for the 8-wave tile kernel (G x ceil(T / 10) of at
-    # least 256 workgroups) with G != 2, and G = 1 on the 4-wave one
+    # prompts long enough for the 8-wave tile kernel (G x ceil(12 T / 128) of
+    # at least 256 workgroups) with G != 2, and G = 1 on the 4-wave one
     inp = qsa_synth.layer_inputs(T, 0, seed=G * 1000 + T, n_groups=G)
     _check(gpu_flash(inp), oracle.attend(inp, None))
 
