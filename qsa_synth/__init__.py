@@ -99,6 +99,62 @@ def layer_inputs(T: int, pos0: int, layer: int = 0, seed: int = SEED, *,
                        ksc=ksc, vq=vq, vsc=vsc, scores=scores)
 
 
+@dataclasses.dataclass
+class SparseHistory:
+    """Inputs over a KV history too long to draw whole: the selected ids of
+    every (token, group) row, and codes and scales for only the cells that
+    some row selects.  cells[g] lists group g's selected cells (sorted,
+    unique); kq[g][i] etc. belong to cell cells[g][i]."""
+
+    T: int
+    pos0: int
+    budget: int
+    n_cells: int
+    q: np.ndarray            # [T][G*HPG][D] float16
+    ids: np.ndarray          # [T][G][budget] int32, each row sorted ascending
+    cells: list              # G arrays of int64
+    kq: list                 # G arrays [len(cells[g])][D] int8
+    ksc: list                # G arrays [len(cells[g])][D/64] float16
+    vq: list
+    vsc: list
+
+
+def sparse_history(T: int, pos0: int, n_cells: int, seed: int = SEED, *, budget: int = BUDGET,
+                   n_groups: int = N_GROUPS, heads_per_group: int = HEADS_PER_GROUP,
+                   head_dim: int = HEAD_DIM, recent: int = 4096,
+                   recent_share: float = 0.25) -> SparseHistory:
+    """Ids and cell data for tokens that all see more than ``budget`` cells.
+
+    Each row takes ``recent_share`` of its budget from its last ``recent``
+    visible cells and the rest from the cells before them (uniform, without
+    replacement), sorted ascending; codes, scales and queries follow the
+    distributions of layer_inputs."""
+    if pos0 + 1 <= budget + recent or n_cells < pos0 + T:
+        raise ValueError("every token must see more than budget + recent cells")
+    rng = np.random.default_rng([seed, T, pos0, n_cells, 41])
+    H = n_groups * heads_per_group
+    nb = head_dim // SCALE_BLOCK
+    q = rng.standard_normal((T, H, head_dim), dtype=np.float32).astype(np.float16)
+    ids = np.empty((T, n_groups, budget), dtype=np.int32)
+    n_recent = int(budget * recent_share)
+    for t in range(T):
+        nkv = pos0 + t + 1
+        for g in range(n_groups):
+            old = rng.choice(nkv - recent, budget - n_recent, replace=False)
+            new = nkv - recent + rng.choice(recent, n_recent, replace=False)
+            ids[t, g] = np.sort(np.concatenate([old, new]))
+    cells, kq, ksc, vq, vsc = [], [], [], [], []
+    for g in range(n_groups):
+        c = np.unique(ids[:, g, :]).astype(np.int64)
+        cells.append(c)
+        kq.append(rng.integers(-127, 128, (len(c), head_dim), dtype=np.int8))
+        ksc.append(rng.uniform(0.002, 0.02, (len(c), nb)).astype(np.float16))
+        vq.append(rng.integers(-127, 128, (len(c), head_dim), dtype=np.int8))
+        vsc.append(rng.uniform(0.002, 0.02, (len(c), nb)).astype(np.float16))
+    return SparseHistory(T=T, pos0=pos0, budget=budget, n_cells=n_cells, q=q, ids=ids,
+                         cells=cells, kq=kq, ksc=ksc, vq=vq, vsc=vsc)
+
+
 def score_rows(T: int, n_groups: int, n_cells: int, seed: int, *, kind: str = "normal",
                levels: int = 4) -> np.ndarray:
     """Selection-score arrays for top-k tests.

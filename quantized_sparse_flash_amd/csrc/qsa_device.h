@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 namespace qsa {
@@ -32,6 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled
 // at compile time (the index stays a constant expression inside f).
@@ -49,6 +51,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // register i of lane l.
 __device__ __forceinline__ f32x4 mfma16(half8_t a, half8_t b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// v_mfma_i32_16x16x64_i8: the same shape with 64 int8 k values, sixteen
+// bytes per lane in A and B (exact int32 accumulation).  A and B hold their
+// k values in the same lane and byte positions, so any fixed assignment of
+// dims to those positions, used by both operands, computes the dot product.
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
 // ------------------------------------------------- int8 -> fp16 convert
@@ -83,15 +92,41 @@ __device__ __forceinline__ half2_t col_pair(uint32_t w_lo, uint32_t w_hi) {
 }
 
 // --------------------------------------------------------- wave helpers
+// Reductions over the four lanes n, n + 16, n + 32, n + 48 on the VALU:
+// v_permlane16_swap with both operands holding v leaves rows (0, 1) of v in
+// one register and rows (1, 0) in the other (likewise rows 2 and 3), so
+// combining the two gives every lane its xor-16 partner's value;
+// v_permlane32_swap does the same for the halves.  Each lane combines the
+// same pair of values in the same order, so all four lanes end with one
+// result.  Written as asm: the compiler's builtin for these swaps, when
+// both results feed one operation, hands that operation the first result
+// twice.  The s_nops give the swap the wait states it needs after the
+// copy and before its results are read.
+template <bool X32>
+__device__ __forceinline__ void swap_pair(float v, float& a, float& b) {
+  a = v;
+  if constexpr (X32)
+    asm("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1"
+        : "+v"(a), "=&v"(b));
+  else
+    asm("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1"
+        : "+v"(a), "=&v"(b));
+}
+__device__ __forceinline__ float xor_pair_max(float v, auto x32) {
+  float a, b;
+  swap_pair<decltype(x32)::value>(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xor_pair_sum(float v, auto x32) {
+  float a, b;
+  swap_pair<decltype(x32)::value>(v, a, b);
+  return a + b;
+}
 __device__ __forceinline__ float wave_max_xor16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  return xor_pair_max(xor_pair_max(v, std::false_type{}), std::true_type{});
 }
 __device__ __forceinline__ float wave_sum_xor16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  return xor_pair_sum(xor_pair_sum(v, std::false_type{}), std::true_type{});
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
