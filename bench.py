@@ -366,14 +366,14 @@ def roofline_of(r: dict, traffic) -> dict:
     tflops = r["flops"] / r["call_s"] / 1e12
     identity = pos0 + T <= r["budget"]
     if kind == "split":
-        kern = "qsa_flash in split mode: flash_rows_kernel<true>"
+        kern = "qsa_flash in split mode: flash_split_kernel"
     elif identity:
         # 8-wave workgroups of 128 queries when at least 256 of them cover
         # the prompt (2 groups), else 4-wave ones of 64
         kern = "qsa_flash: dequant_chunks_kernel + flash_tile_kernel<%d>" % (
             8 if 2 * -(-T * 12 // 128) >= 256 else 4)
     else:
-        kern = "qsa_flash: flash_rows_kernel<false>"
+        kern = "qsa_flash: flash_rows_staged_kernel<false>"
     roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
             "traffic": traffic, "kernel": kern, "flops_per_launch": r["flops"],
@@ -389,8 +389,10 @@ def roofline_of(r: dict, traffic) -> dict:
     if not identity:
         # rows above budget gather their own cells: mostly from L2 and the
         # Infinity Cache (the gathered bytes exceed what HBM could deliver)
-        roof["note"] = ("row gather: neither roofline binds; the gather latency from L2 and "
-                        "the Infinity Cache does (see gathered and traffic)")
+        roof["note"] = ("row gather: neither roofline binds; each row's cells are copied from "
+                        "L2 and the Infinity Cache into LDS (see gathered and traffic) while "
+                        "the VALU widens V to fp16; QK^T runs on the int8 MFMA, priced here "
+                        "at the fp16 peak")
     return roof
 
 
