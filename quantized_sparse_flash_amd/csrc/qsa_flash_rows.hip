@@ -222,7 +222,8 @@ void flash_split_kernel(RowArgs a) {
 // sq = max|q| / 127 over the row), every 64-dim block gives the exact
 // integer products 256 I_hi + I_lo, and the cell's K scale of that block
 // multiplies them in fp32.  The scores are exact in K and within sq / 512
-// per element in Q, tighter than rounding each k = code * scale to fp16.
+// per element in Q (sq / 256 where the low piece saturates at 127), tighter
+// than rounding each k = code * scale to fp16.
 // PV keeps the fp16 MFMA with P rounded to fp16.
 //
 // Image of a wave (17,152 bytes): K codes | K scales | V codes | V scales |
