@@ -9,8 +9,10 @@ never imports it; the two meet only in the seeded input generator
 Two independent formulations live here:
   * ``qsa_oracle.c`` (built with gcc, OpenMP over (token, group) rows): the
     plain definition -- selection, then exact softmax attention over the
-    selected cells -- plus the chunk-partial and log-sum-exp merge steps,
-    and the K/V quantiser that fills the int8 cache (decided in IEEE fp32);
+    selected cells -- plus the selection scores (the reading of the
+    score kernel: an fp64 dot product of index query and pooled key), the
+    chunk-partial and log-sum-exp merge steps, and the K/V quantiser that
+    fills the int8 cache (decided in IEEE fp32);
   * ``dense_reference`` below: a numpy brute force over the full (token x
     cell) matrix with explicit causal and top-k masks, for tiny inputs.
 
@@ -58,13 +60,14 @@ def _load():
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.qsa_oracle_select.argtypes = [i32, i32, i32, i32, i64, P, P]
+    lib.qsa_oracle_score.argtypes = [i32, i32, i32, i32, i32, i64, P, P, P]
     lib.qsa_oracle_attend.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, P, P, P, P, P, P]
     lib.qsa_oracle_partials.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32,
                                         P, P, P, P, P, P, P, P, P]
     lib.qsa_oracle_merge.argtypes = [i32, i32, i32, i32, P, P, P]
     lib.qsa_oracle_quantize.argtypes = [i64, i32, i32, P, P, P]
     lib.qsa_oracle_f32_to_f16.argtypes = [i64, P, P]
-    for f in (lib.qsa_oracle_select, lib.qsa_oracle_attend, lib.qsa_oracle_partials,
+    for f in (lib.qsa_oracle_select, lib.qsa_oracle_score, lib.qsa_oracle_attend, lib.qsa_oracle_partials,
               lib.qsa_oracle_merge, lib.qsa_oracle_quantize, lib.qsa_oracle_f32_to_f16):
         f.restype = ctypes.c_int
     _lib = lib
@@ -82,6 +85,22 @@ def _c(a, dtype):
 def n_selected(pos0: int, t: int, budget: int) -> int:
     """Cells token t attends: all pos0+t+1 visible cells, capped at budget."""
     return min(pos0 + t + 1, budget)
+
+
+def score(T: int, pos0: int, budget: int, qidx: np.ndarray, pooled: np.ndarray) -> np.ndarray:
+    """Selection scores [T][G][n_cells] (fp64) of the rows above budget at
+    their visible cells; NaN everywhere else.  qidx [T][G][D], pooled
+    [G][n_cells][D]."""
+    lib = _load()
+    G, n_cells, D = pooled.shape
+    if qidx.shape != (T, G, D):
+        raise ValueError("qidx shape")
+    out = np.full((T, G, n_cells), np.nan, dtype=np.float64)
+    rc = lib.qsa_oracle_score(T, pos0, G, D, budget, n_cells, _ptr(_c(qidx, np.float64)),
+                              _ptr(_c(pooled, np.float64)), _ptr(out))
+    if rc != 0:
+        raise RuntimeError("qsa_oracle_score failed")
+    return out
 
 
 def select(T: int, pos0: int, budget: int, scores: Optional[np.ndarray], n_groups: int,

@@ -49,6 +49,36 @@ static int by_int_asc(const void *pa, const void *pb) {
   return (a > b) - (a < b);
 }
 
+/* Selection scores.  The pages name the score kernel and its buffers
+ * ("sol_r27_qsa", decision: four-value dot products; correctness: qidx,
+ * pooled, scores) but not their content; the reading taken: the score of
+ * cell c for token t in group g is the dot product of the token's index
+ * query with the cell's pooled key,
+ *   scores[t][g][c] = sum_d qidx[t][g][d] * pooled[g][c][d],
+ * written for the rows above budget (n > budget, the rows whose selection
+ * reads scores) at cells c < n; every other element is left as it was.
+ * fp64 throughout (fp32 inputs widen exactly, and their products are exact
+ * in fp64). */
+int qsa_oracle_score(int T, int pos0, int G, int D, int budget, int64_t n_cells,
+                     const double *qidx, const double *pooled, double *scores) {
+  if (T < 0 || pos0 < 0 || G <= 0 || D <= 0 || budget <= 0 || n_cells < (int64_t)pos0 + T)
+    return ORACLE_BAD;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < T * G; ++r) {
+    int t = r / G, g = r % G;
+    int64_t n = (int64_t)pos0 + t + 1;
+    if (n <= budget) continue;
+    const double *q = qidx + (int64_t)r * D;
+    for (int64_t c = 0; c < n; ++c) {
+      const double *p = pooled + ((int64_t)g * n_cells + c) * D;
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d) acc += q[d] * p[d];
+      scores[(int64_t)r * n_cells + c] = acc;
+    }
+  }
+  return ORACLE_OK;
+}
+
 /* Selected ids of every (t, g) row: ids[t][g][0..budget), identity rows
  * 0..n-1 then -1, above-budget rows exactly `budget` ascending ids.
  * scores is [T][G][n_cells] and is read only for rows with n > budget

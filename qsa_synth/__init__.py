@@ -155,6 +155,19 @@ def sparse_history(T: int, pos0: int, n_cells: int, seed: int = SEED, *, budget:
                          cells=cells, kq=kq, ksc=ksc, vq=vq, vsc=vsc)
 
 
+def score_inputs(T: int, pos0: int, index_dim: int = 4, seed: int = SEED, *,
+                 n_groups: int = N_GROUPS, n_cells: Optional[int] = None) -> tuple:
+    """Inputs of the selection-score step: qidx [T][G][index_dim] and pooled
+    [G][n_cells][index_dim], both N(0,1) fp32 (this build's recipe; the
+    pages name the buffers, not their distributions)."""
+    if n_cells is None:
+        n_cells = pos0 + T
+    rng = np.random.default_rng([seed, T, pos0, index_dim, 43])
+    qidx = rng.standard_normal((T, n_groups, index_dim), dtype=np.float32)
+    pooled = rng.standard_normal((n_groups, n_cells, index_dim), dtype=np.float32)
+    return qidx, pooled
+
+
 def score_rows(T: int, n_groups: int, n_cells: int, seed: int, *, kind: str = "normal",
                levels: int = 4) -> np.ndarray:
     """Selection-score arrays for top-k tests.

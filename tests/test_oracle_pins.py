@@ -256,3 +256,68 @@ def test_partials_chunk_max_and_sum_definitions():
             blk = s[64 * kk:64 * kk + 64]
             assert m[0, kk, h] == pytest.approx(blk.max(), rel=1e-14)
             assert l[0, kk, h] == pytest.approx(np.exp(blk - blk.max()).sum(), rel=1e-13)
+
+
+# ---- selection scores (the reading of "sol_r27_qsa": qidx . pooled per cell)
+
+def test_score_agrees_with_a_python_sum():
+    """Every score of the rows above budget equals the dot product summed
+    term by term in Python floats; spare cells past n_kv stay unwritten."""
+    T, pos0, budget, D = 5, 40, 16, 12
+    n_cells = pos0 + T + 5
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((T, 2, D)).astype(np.float32)
+    p = rng.standard_normal((2, n_cells, D)).astype(np.float32)
+    got = oracle.score(T, pos0, budget, q, p)
+    for t in range(T):
+        n = pos0 + t + 1
+        for g in range(2):
+            want = [sum(float(q[t, g, d]) * float(p[g, c, d]) for d in range(D)) for c in range(n)]
+            np.testing.assert_allclose(got[t, g, :n], want, rtol=1e-13, atol=1e-13)
+            assert np.isnan(got[t, g, n:]).all()
+
+
+def test_score_rows_under_budget_are_not_written():
+    """Rows that see at most budget cells take identity ids and need no
+    scores: the oracle leaves them as they were."""
+    T, pos0, budget, D = 8, 10, 14, 4   # tokens 0..3 see <= 14 cells
+    q = np.ones((T, 2, D), np.float32)
+    p = np.ones((2, pos0 + T, D), np.float32)
+    got = oracle.score(T, pos0, budget, q, p)
+    for t in range(T):
+        n = pos0 + t + 1
+        if n <= budget:
+            assert np.isnan(got[t]).all()
+        else:
+            assert (got[t, :, :n] == D).all() and np.isnan(got[t, :, n:]).all()
+
+
+def test_score_closed_form_of_unit_keys():
+    """pooled[g][c] = (c + 1) e_{(c + g) mod D}: the score picks one element
+    of the index query, scaled exactly -- a wrong cell, group or element
+    index, or a transposed operand, changes it."""
+    T, pos0, budget, D = 3, 70, 20, 8
+    n_cells = pos0 + T
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((T, 2, D)).astype(np.float32)
+    p = np.zeros((2, n_cells, D), np.float32)
+    for g in range(2):
+        for c in range(n_cells):
+            p[g, c, (c + g) % D] = c + 1
+    got = oracle.score(T, pos0, budget, q, p)
+    for t in range(T):
+        for g in range(2):
+            n = pos0 + t + 1
+            want = np.array([(c + 1) * float(q[t, g, (c + g) % D]) for c in range(n)])
+            assert np.array_equal(got[t, g, :n], want)
+
+
+def test_score_is_linear_in_the_index_query():
+    T, pos0, budget, D = 4, 30, 8, 16
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((T, 2, D)).astype(np.float32)
+    p = rng.standard_normal((2, pos0 + T, D)).astype(np.float32)
+    a = oracle.score(T, pos0, budget, q, p)
+    b = oracle.score(T, pos0, budget, 2 * q, p)
+    ok = ~np.isnan(a)
+    assert np.array_equal(b[ok], 2 * a[ok])
