@@ -26,7 +26,9 @@ Other workloads (--workload):
   t1984_pos30000_split            the long-context prompt through the same
                                   split path instead of the fused one;
   quantize_kv_31984               the K/V quantiser on the long-context
-                                  cache (cells quantised per second).
+                                  cache (cells quantised per second);
+  score_t1984_pos30000            the selection scores of the long-context
+                                  prompt (qsa_score, four values per cell).
 
 One JSON line goes to stdout; progress goes to stderr.  Every C-ABI call of
 a step is bound once (arguments checked and marshalled before timing) and
@@ -92,6 +94,7 @@ WORKLOADS = {
     "decode8_pos30000": dict(T=8, pos0=30000, layers=1, kind="split"),
     "t1984_pos30000_split": dict(T=1984, pos0=30000, layers=1, kind="split"),
     "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
+    "score_t1984_pos30000": dict(T=1984, pos0=30000, layers=1, kind="score"),
 }
 # the default line also reports these (12 layers each, same protocol)
 OTHER_PROMPTS = ("t512_pos0_x12", "t1024_pos0_x12")
@@ -104,6 +107,8 @@ FLUSH_BYTES = 1 << 30  # written before each sample: 4x the Infinity Cache
 DECODE_REPEAT = 16  # split qsa_flash launches per kernel-timing step (decode)
 QUANT_REPEAT = 8    # K and V qsa_quantize launch pairs per kernel-timing step
 QUANT_ROW_BYTES = 256 * 2 + 256 + 4 * 2  # fp16 row in; int8 codes + 4 fp16 scales out
+SCORE_INDEX_DIM = 4  # qsa_score vector length of the score workload (one value per 64-dim block)
+SCORE_REPEAT = 8     # qsa_score launches per kernel-timing step
 # sources of the kernels whose HBM traffic each workload's record describes
 TRAFFIC_SOURCES = {
     "t1984_pos0_x12": ("qsa_flash_tile.hip", "qsa_device.h"),
@@ -437,6 +442,9 @@ def main():
     if WORKLOADS[args.workload]["kind"] == "quantize":
         bench_quantize(args, WORKLOADS[args.workload], dev)
         return
+    if WORKLOADS[args.workload]["kind"] == "score":
+        bench_score(args, WORKLOADS[args.workload], dev)
+        return
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
     r = measure(args.workload, args, dev, flush)
@@ -595,6 +603,87 @@ def bench_quantize(args, wl, dev) -> None:
                                 "sample": "%d passes of the oracle quantiser over the K rows "
                                           "(%d rows, single thread), %.1f s; scaled to K+V "
                                           "cells" % (done, rows, t_total)}
+    print(json.dumps(line), flush=True)
+
+
+def bench_score(args, wl, dev) -> None:
+    """qsa_score for one long-context layer: the rows above budget get a
+    score per visible cell from a SCORE_INDEX_DIM-value index query and
+    pooled key; one call per step."""
+    import torch
+
+    import qsa_synth
+    import quantized_sparse_flash_amd as qsa
+
+    T, pos0, D, G, budget = wl["T"], wl["pos0"], SCORE_INDEX_DIM, 2, qsa_synth.BUDGET
+    n_cells = pos0 + T
+    log("bench: generating score inputs (T=%d pos0=%d, %d values per cell)" % (T, pos0, D))
+    qidx_h, pooled_h = qsa_synth.score_inputs(T, pos0, D)
+    qidx, pooled = torch.from_numpy(qidx_h).to(dev), torch.from_numpy(pooled_h).to(dev)
+    scores = torch.empty((T, G, n_cells), dtype=torch.float32, device=dev)
+    shape = qsa.QsaShape(T=T, pos0=pos0, n_groups=G, budget=budget, n_cells=n_cells)
+    call = qsa.bind_qsa_score(shape, qidx, pooled, scores)
+    n_scores = sum(G * (pos0 + t + 1) for t in range(T) if pos0 + t + 1 > budget)
+    by = n_scores * 4 + qidx_h.nbytes + pooled_h.nbytes  # scores out, inputs read once
+    flops = n_scores * 2 * D
+
+    n_warm, steps = run_warmup(args, call, torch.cuda.synchronize)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tm = Timer(torch)
+    ev = [tm.pair() for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record()
+        for _ in range(SCORE_REPEAT):
+            call()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    mean_launch_s = sum(e0.elapsed_time(e1) for e0, e1 in ev) / (SCORE_REPEAT * steps) / 1e3
+    gbs = by / mean_launch_s / 1e9
+    log("bench: %s %.3f ms/step, qsa_score kernel mean %.1f us, %.0f GB/s"
+        % (args.workload, elapsed / steps * 1e3, mean_launch_s * 1e6, gbs))
+    line = {
+        "metric": "qsa_score query-tokens/s at T=%d (1 layer)" % T,
+        "value": T * steps / elapsed,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": n_warm,
+        "ms_per_step": elapsed / steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "precision": "fp32 index queries and pooled keys, fp32 fused multiply-adds",
+        "data": "synthetic (seeded: qidx and pooled N(0,1) fp32)",
+        "config": {"workload": "%s: qsa_score, T=%d pos0=%d, 2 KV groups, %d values per cell, "
+                               "budget %d" % (args.workload, T, pos0, D, budget),
+                   "T": T, "pos0": pos0, "n_groups": G, "index_dim": D, "budget": budget},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "score_kernel (qsa_score)",
+                     "algorithmic_bytes_per_launch": by, "scores_per_launch": n_scores,
+                     "flops_per_launch": flops, "mean_launch_us": mean_launch_s * 1e6,
+                     "launch_timing": "HIP events around %d back-to-back qsa_score calls per "
+                                      "step, over a timed region of its own" % SCORE_REPEAT},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("bench: timing the CPU oracle's scores (bounded sample)")
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        done, t_total = 0, 0.0
+        while done < 10 and t_total < 8.0:
+            t1 = time.perf_counter()
+            oracle.score(T, pos0, budget, qidx_h, pooled_h)
+            t_total += time.perf_counter() - t1
+            done += 1
+        line["cpu_baseline"] = {"value": T * done / t_total, "unit": "query-tokens/s (1 layer)",
+                                "cores": threads, "kind": "oracle",
+                                "sample": "%d whole calls of the workload, fp64 oracle scores, "
+                                          "%.1f s wall" % (done, t_total)}
     print(json.dumps(line), flush=True)
 
 

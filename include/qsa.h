@@ -57,6 +57,7 @@ extern "C" {
 #define QSA_CHUNK 64           /* selected cells per chunk / partial record */
 #define QSA_PART_STRIDE 258    /* floats per partial record: o[256], m, l */
 #define QSA_MAX_BUDGET 65536   /* largest supported budget */
+#define QSA_MAX_INDEX_DIM 256  /* longest qsa_score vectors */
 #define QSA_DEFAULT_BUDGET 2051
 #define QSA_NOALLOC_SCRATCH_BYTES (16 << 20) /* device scratch held by qsa_flash_noalloc */
 
@@ -71,6 +72,36 @@ typedef struct {
   int64_t n_cells;         /* KV cells held per group (>= pos0 + T); also the
                               row stride of `scores` */
 } qsa_shape;
+
+/*
+ * qsa_score -- selection scores, the step before qsa_topk.  The pages name
+ * the score kernel and its buffers (page "round 27 track b - qsa prep and
+ * merge", decision: its four-value dot products are fully unrolled;
+ * correctness: the qidx, pooled and scores buffers; page "round 6 track b -
+ * qsa flash", actual runs: a worst relative score difference of 2.76e-6)
+ * but not what qidx and pooled hold.  This library's reading: the score of
+ * cell c for token t in group g is the dot product of the token's index
+ * query with the cell's pooled key,
+ *     scores[t][g][c] = sum over d of qidx[t][g][d] * pooled[g][c][d],
+ * in fp32, one fused multiply-add per d in ascending order.
+ *
+ *   index_dim : length of both vectors, a multiple of 4 in
+ *               [4, QSA_MAX_INDEX_DIM] (4: one value per 64-dim block).
+ *   qidx      : device, const float [T][G][index_dim].
+ *   pooled    : device, const float [G][n_cells][index_dim].
+ *   scores    : device, float [T][G][n_cells] (the layout qsa_topk reads).
+ *               Row (t, g) is written at cells [0, n_kv(t)) when
+ *               n_kv(t) > budget, the rows whose selection reads scores;
+ *               every other element is left as it was.  When no row is
+ *               above budget nothing is read or written and the pointers
+ *               may be NULL.
+ * Alignment: 16 bytes for qidx, pooled and scores.  Errors:
+ * QSA_ERR_UNSUPPORTED (index_dim), QSA_ERR_SHAPE, QSA_ERR_ARG.
+ * Numerics: |score - exact| <= index_dim * 2^-24 * sum_d |qidx_d pooled_d|
+ * to first order (recursive fp32 summation with fused multiply-adds).
+ */
+int qsa_score(const qsa_shape *shape, int32_t index_dim, const float *qidx, const float *pooled,
+              float *scores, void *stream);
 
 /*
  * qsa_topk -- step 1: selected ids of every (token, group) row.
@@ -119,8 +150,11 @@ int qsa_topk(const qsa_shape *shape, const float *scores, int32_t *ids, void *st
  *              written.
  * Alignment: 16 bytes for q, kq, vq, out and part; 8 for ksc, vsc; 4 for ids;
  * 256 for workspace.
- * Numerics: fp16 MFMA products with fp32 accumulation; relative L2 error
- * against exact attention about 4e-4 on the pages' value ranges.
+ * Numerics: fp16 MFMA products with fp32 accumulation (for rows above
+ * budget the scores come from exact int8 products of the K codes with q
+ * split into two int8 pieces, each element of q then within 2^-15 of the
+ * head's largest |q|); relative L2 error against exact attention about
+ * 4e-4 on the pages' value ranges.
  */
 int qsa_flash(const qsa_shape *shape, const _Float16 *q, const int8_t *kq, const _Float16 *ksc,
               const int8_t *vq, const _Float16 *vsc, const int32_t *ids, _Float16 *out,

@@ -41,10 +41,11 @@ CHUNK = 64
 PART_STRIDE = 258
 DEFAULT_BUDGET = 2051
 MAX_BUDGET = 65536
+MAX_INDEX_DIM = 256  # longest qsa_score vectors
 
-EXPORTED = ("qsa_topk", "qsa_flash", "qsa_flash_prepare", "qsa_flash_attend", "qsa_merge",
-            "qsa_quantize", "qsa_status_string", "qsa_part_elems", "qsa_flash_workspace_bytes",
-            "qsa_flash_noalloc")
+EXPORTED = ("qsa_score", "qsa_topk", "qsa_flash", "qsa_flash_prepare", "qsa_flash_attend",
+            "qsa_merge", "qsa_quantize", "qsa_status_string", "qsa_part_elems",
+            "qsa_flash_workspace_bytes", "qsa_flash_noalloc")
 
 
 class QsaError(RuntimeError):
@@ -103,6 +104,7 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     SP = ctypes.POINTER(_CShape)
+    lib.qsa_score.argtypes = [SP, ctypes.c_int32, P, P, P, P]
     lib.qsa_topk.argtypes = [SP, P, P, P]
     lib.qsa_flash.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]
     lib.qsa_flash_prepare.argtypes = [SP, P, P, P, P, P, ctypes.c_int64, P]
@@ -116,8 +118,8 @@ def load_library(path: str = LIB_PATH):
     lib.qsa_status_string.restype = ctypes.c_char_p
     lib.qsa_part_elems.argtypes = [SP]
     lib.qsa_part_elems.restype = ctypes.c_int64
-    for f in (lib.qsa_topk, lib.qsa_flash, lib.qsa_flash_prepare, lib.qsa_flash_attend,
-              lib.qsa_merge, lib.qsa_quantize, lib.qsa_flash_noalloc):
+    for f in (lib.qsa_score, lib.qsa_topk, lib.qsa_flash, lib.qsa_flash_prepare,
+              lib.qsa_flash_attend, lib.qsa_merge, lib.qsa_quantize, lib.qsa_flash_noalloc):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -176,6 +178,29 @@ def _dev_ptr(t, name, dtype, shape=None):
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _score_args(s: QsaShape, qidx, pooled, scores) -> list:
+    import torch
+    if qidx is None or qidx.dim() != 3:
+        raise ValueError("qidx must be a [T][G][index_dim] float32 device tensor")
+    dim = int(qidx.shape[2])
+    return [ctypes.c_int32(dim),
+            _dev_ptr(qidx, "qidx", torch.float32, (s.T, s.n_groups, dim)),
+            _dev_ptr(pooled, "pooled", torch.float32, (s.n_groups, s.n_cells, dim)),
+            _dev_ptr(scores, "scores", torch.float32, (s.T, s.n_groups, s.n_cells))]
+
+
+def qsa_score(shape: QsaShape, qidx, pooled, scores, stream=None) -> None:
+    """Selection scores of the rows above budget: scores[t][g][c] =
+    qidx[t][g] . pooled[g][c] (fp32) for c < n_kv(t); index_dim is
+    qidx.shape[2]."""
+    s = shape
+    cs = s.c()
+    rc = load_library().qsa_score(ctypes.byref(cs), *_score_args(s, qidx, pooled, scores),
+                                  _stream(stream))
+    if rc != QSA_OK:
+        raise QsaError(rc, "qsa_score")
 
 
 def qsa_topk(shape: QsaShape, scores, ids, stream=None) -> None:
@@ -357,6 +382,14 @@ def bind_qsa_flash(shape: QsaShape, q, kq, ksc, vq, vsc, ids, out, part=None, wo
             _stream(stream)]
     return BoundCall(load_library().qsa_flash, "qsa_flash", args,
                      (cs, q, kq, ksc, vq, vsc, ids, out, part, workspace))
+
+
+def bind_qsa_score(shape: QsaShape, qidx, pooled, scores, stream=None) -> BoundCall:
+    """qsa_score with the arguments of ``qsa_score`` (checked here, once)."""
+    s = shape
+    cs = s.c()
+    args = [ctypes.byref(cs)] + _score_args(s, qidx, pooled, scores) + [_stream(stream)]
+    return BoundCall(load_library().qsa_score, "qsa_score", args, (cs, qidx, pooled, scores))
 
 
 def bind_qsa_topk(shape: QsaShape, scores, ids, stream=None) -> BoundCall:

@@ -72,6 +72,20 @@ int64_t qsa_part_elems(const qsa_shape* s) {
   return (int64_t)s->T * kc * s->n_groups * QSA_HEADS_PER_GROUP * QSA_PART_STRIDE;
 }
 
+int qsa_score(const qsa_shape* s, int32_t index_dim, const float* qidx, const float* pooled,
+              float* scores, void* stream) {
+  int rc = check_shape(s);
+  if (rc != QSA_OK) return rc;
+  if (index_dim < 4 || index_dim > QSA_MAX_INDEX_DIM || index_dim % 4 != 0)
+    return QSA_ERR_UNSUPPORTED;
+  if (!any_above_budget(s)) return QSA_OK;  // no row reads scores
+  if (!qidx || !pooled || !scores) return QSA_ERR_ARG;
+  if (!aligned(qidx, 16) || !aligned(pooled, 16) || !aligned(scores, 16)) return QSA_ERR_ARG;
+  return launch_status(qsa::launch_score(qidx, pooled, scores, s->T, s->pos0, s->n_groups,
+                                         s->budget, s->n_cells, index_dim,
+                                         (hipStream_t)stream));
+}
+
 int qsa_topk(const qsa_shape* s, const float* scores, int32_t* ids, void* stream) {
   int rc = check_shape(s);
   if (rc != QSA_OK) return rc;

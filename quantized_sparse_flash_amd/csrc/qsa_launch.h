@@ -20,6 +20,9 @@ struct RowArgs {
   int64_t n_cells;
 };
 
+// Selection scores of the rows above budget: scores[t][g][c] for c < n_kv(t).
+hipError_t launch_score(const float* qidx, const float* pooled, float* scores, int T, int pos0,
+                        int G, int budget, int64_t n_cells, int dim, hipStream_t stream);
 hipError_t launch_topk(const float* scores, int32_t* ids, int T, int pos0, int G, int budget,
                        int64_t n_cells, hipStream_t stream);
 hipError_t launch_merge(const float* part, _Float16* out, int T, int H, int pos0, int budget,

@@ -1,0 +1,163 @@
+// qsa_score.hip -- selection scores: the step before the top-k.
+//
+// Pages: "round 27 track b - qsa prep and merge" (decision: the score
+// kernel's four-value dot products are fully unrolled; correctness: the
+// qidx, pooled and scores buffers) and "round 6 track b - qsa flash" (actual
+// runs: worst relative score difference 2.76e-6).  Reading: the score of
+// cell c for token t in group g is the fp32 dot product of the token's index
+// query qidx[t][g][:] with the cell's pooled key pooled[g][c][:], one fused
+// multiply-add per element in ascending order.
+//
+// Work mapping (gfx950, wave64).  A 256-thread workgroup covers a
+// 4096-cell stretch of a row, 16 cells per thread; cells past a row are
+// clamped for the load and not stored.
+//   * score4_kernel (index_dim 4, the workload's width): a workgroup holds
+//     its cells' pooled keys in registers (64 VGPRs per thread) and scores
+//     them for a block of 16 tokens of one group, each token's index query
+//     read through scalar loads, so the pooled keys are read once per 16
+//     rows.  Thread i takes the cells 1024 p + 4 i .. + 3, p < 4, and
+//     stores each group of four as one 16-byte vector when the row is
+//     16-byte aligned (n_cells a multiple of 4), else one by one.
+//   * score_kernel (any index_dim): one workgroup per (token, group) row and
+//     stretch, thread i taking cells i + 256 k, so each of a wave's loads
+//     and stores covers one contiguous span; the dot product accumulates in
+//     steps of four values.
+// Only rows above budget are written (their top-k reads them).  At the
+// long-context shape the kernels write ~0.5 GB of scores: they are bound by
+// those HBM writes.
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+namespace qsa {
+
+constexpr int kScoreThreads = 256;
+constexpr int kScorePasses = 16;  // cells per thread, 256 apart
+constexpr int kScoreCellsPerBlock = kScoreThreads * kScorePasses;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kScoreThreads)
+void score_kernel(const float* __restrict__ qidx, const float* __restrict__ pooled,
+                  float* __restrict__ scores, int T, int pos0, int G, int budget, int64_t n_cells,
+                  int dim) {
+  const int64_t base = (int64_t)blockIdx.x * kScoreCellsPerBlock + threadIdx.x;
+  // rows t * G + g, strided by the grid's height (at most 65535)
+  for (int row = blockIdx.y; row < T * G; row += gridDim.y) {
+    const int t = row / G, g = row % G;
+    const int64_t nkv = (int64_t)pos0 + t + 1;
+    if (nkv <= (int64_t)budget) continue;  // identity row: its scores are never read
+    if ((int64_t)blockIdx.x * kScoreCellsPerBlock >= nkv) continue;
+    const float* q = qidx + (int64_t)row * dim;
+    const float* pg = pooled + (int64_t)g * n_cells * dim;
+    float* out = scores + (int64_t)row * n_cells;
+
+    float acc[kScorePasses];
+#pragma unroll
+    for (int k = 0; k < kScorePasses; ++k) acc[k] = 0.f;
+    for (int d = 0; d < dim; d += 4) {
+      const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(q + d);
+      f32x4_t pv[kScorePasses];
+#pragma unroll
+      for (int k = 0; k < kScorePasses; ++k) {
+        const int64_t c = base + (int64_t)kScoreThreads * k;
+        const int64_t cl = c < nkv ? c : nkv - 1;  // in the row, read and dropped
+        pv[k] = *reinterpret_cast<const f32x4_t*>(pg + cl * dim + d);
+      }
+#pragma unroll
+      for (int k = 0; k < kScorePasses; ++k) {
+        acc[k] = __builtin_fmaf(qv.x, pv[k].x, acc[k]);
+        acc[k] = __builtin_fmaf(qv.y, pv[k].y, acc[k]);
+        acc[k] = __builtin_fmaf(qv.z, pv[k].z, acc[k]);
+        acc[k] = __builtin_fmaf(qv.w, pv[k].w, acc[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kScorePasses; ++k) {
+      const int64_t c = base + (int64_t)kScoreThreads * k;
+      if (c < nkv) out[c] = acc[k];
+    }
+  }
+}
+
+constexpr int kScore4Tokens = 16;  // tokens per score4_kernel workgroup
+
+__global__ __launch_bounds__(kScoreThreads)
+void score4_kernel(const float* __restrict__ qidx, const float* __restrict__ pooled,
+                   float* __restrict__ scores, int T, int pos0, int G, int budget,
+                   int64_t n_cells) {
+  const int g = blockIdx.y % G;
+  const int t0 = (blockIdx.y / G) * kScore4Tokens;
+  const int t_end = min(t0 + kScore4Tokens, T);
+  const int64_t nkv_max = (int64_t)pos0 + t_end;  // the block's last token sees most
+  if (nkv_max <= (int64_t)budget) return;         // identity rows only
+  const int64_t stretch = (int64_t)blockIdx.x * kScoreCellsPerBlock;
+  if (stretch >= nkv_max) return;
+  // pass k: cells stretch + 1024 k + 4 i .. + 3 (one 16-byte store each)
+  const int64_t base = stretch + 4 * threadIdx.x;
+  const float* pg = pooled + (int64_t)g * n_cells * 4;
+  f32x4_t pv[kScorePasses];
+#pragma unroll
+  for (int k = 0; k < kScorePasses; ++k) {
+    const int64_t c = base + 1024 * (k >> 2) + (k & 3);
+    const int64_t cl = c < nkv_max ? c : nkv_max - 1;  // in the cache, read and dropped
+    pv[k] = *reinterpret_cast<const f32x4_t*>(pg + cl * 4);
+  }
+  const bool vec_store = (n_cells & 3) == 0;  // every row starts 16-byte aligned
+  // the block's index queries, all requested before the first is needed
+  f32x4_t qs[kScore4Tokens];
+#pragma unroll
+  for (int u = 0; u < kScore4Tokens; ++u) {
+    const int tl = min(t0 + u, T - 1);  // in bounds; rows past T are not stored
+    qs[u] = *reinterpret_cast<const f32x4_t*>(qidx + ((int64_t)tl * G + g) * 4);
+  }
+#pragma unroll
+  for (int u = 0; u < kScore4Tokens; ++u) {
+    const int t = t0 + u;
+    const f32x4_t qv = qs[u];
+    const int64_t nkv = (int64_t)pos0 + t + 1;
+    if (t >= T || nkv <= (int64_t)budget || stretch >= nkv) continue;
+    float* out = scores + ((int64_t)t * G + g) * n_cells;
+#pragma unroll
+    for (int p = 0; p < kScorePasses / 4; ++p) {
+      float acc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x4_t pk = pv[4 * p + e];
+        acc[e] = __builtin_fmaf(qv.x, pk.x, 0.f);
+        acc[e] = __builtin_fmaf(qv.y, pk.y, acc[e]);
+        acc[e] = __builtin_fmaf(qv.z, pk.z, acc[e]);
+        acc[e] = __builtin_fmaf(qv.w, pk.w, acc[e]);
+      }
+      const int64_t c0 = base + 1024 * p;
+      if (vec_store && c0 + 4 <= nkv) {
+        *reinterpret_cast<f32x4_t*>(out + c0) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c0 + e < nkv) out[c0 + e] = acc[e];
+      }
+    }
+  }
+}
+
+hipError_t launch_score(const float* qidx, const float* pooled, float* scores, int T, int pos0,
+                        int G, int budget, int64_t n_cells, int dim, hipStream_t stream) {
+  const int64_t max_nkv = (int64_t)pos0 + T;
+  const int64_t blocks = (max_nkv + kScoreCellsPerBlock - 1) / kScoreCellsPerBlock;
+  const int64_t rows = (int64_t)T * G;
+  if (dim == 4) {
+    const int64_t tblocks = (T + kScore4Tokens - 1) / kScore4Tokens * G;
+    if (tblocks <= 65535) {
+      dim3 grid((unsigned)blocks, (unsigned)tblocks), block(kScoreThreads);
+      score4_kernel<<<grid, block, 0, stream>>>(qidx, pooled, scores, T, pos0, G, budget,
+                                                n_cells);
+      return hipGetLastError();
+    }
+  }
+  dim3 grid((unsigned)blocks, (unsigned)(rows < 65535 ? rows : 65535)), block(kScoreThreads);
+  score_kernel<<<grid, block, 0, stream>>>(qidx, pooled, scores, T, pos0, G, budget, n_cells,
+                                           dim);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

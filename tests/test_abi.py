@@ -161,6 +161,30 @@ def test_quantize_arguments_are_validated():
     assert q(4, 256, A, A, 0) == qsa.QSA_ERR_ARG
 
 
+def test_score_arguments_are_validated():
+    lib = qsa.load_library()
+    A = 0x10000
+    under = qsa.QsaShape(T=8, pos0=0)
+    over = qsa.QsaShape(T=8, pos0=2050)
+    assert qsa.MAX_INDEX_DIM == _header_defines()["QSA_MAX_INDEX_DIM"]
+
+    def sc(shape, dim, qi, po, out):
+        cs = shape.c()
+        v = lambda x: ctypes.c_void_p(x) if x else None
+        return lib.qsa_score(ctypes.byref(cs), dim, v(qi), v(po), v(out), None)
+
+    assert sc(under, 4, 0, 0, 0) == qsa.QSA_OK                    # no row reads scores
+    for dim in (0, 2, 6, qsa.MAX_INDEX_DIM + 4):
+        assert sc(over, dim, A, A, A) == qsa.QSA_ERR_UNSUPPORTED
+    assert sc(qsa.QsaShape(T=0, pos0=0), 4, A, A, A) == qsa.QSA_ERR_SHAPE
+    assert sc(over, 4, 0, A, A) == qsa.QSA_ERR_ARG                # qidx
+    assert sc(over, 4, A, 0, A) == qsa.QSA_ERR_ARG                # pooled
+    assert sc(over, 4, A, A, 0) == qsa.QSA_ERR_ARG                # scores
+    assert sc(over, 4, A + 8, A, A) == qsa.QSA_ERR_ARG            # 16 B alignment
+    assert sc(over, 4, A, A + 4, A) == qsa.QSA_ERR_ARG
+    assert sc(over, 4, A, A, A + 4) == qsa.QSA_ERR_ARG
+
+
 def test_page_case_lists_hold_the_pages_counts():
     # the GPU parity tests take their cases from these lists: the r9 result's
     # 13 byte-checked cases, the r14 16-case grid, the r27 40-case matrix
