@@ -114,6 +114,7 @@ TRAFFIC_SOURCES = {
     "t1984_pos0_x12": ("qsa_flash_tile.hip", "qsa_device.h"),
     "t1984_pos30000": ("qsa_flash_rows.hip", "qsa_device.h"),
     "quantize_kv_31984": ("qsa_quantize.hip", "qsa_device.h"),
+    "score_t1984_pos30000": ("qsa_score.hip", "qsa_device.h"),
 }
 
 
@@ -663,8 +664,9 @@ def bench_score(args, wl, dev) -> None:
                                "budget %d" % (args.workload, T, pos0, D, budget),
                    "T": T, "pos0": pos0, "n_groups": G, "index_dim": D, "budget": budget},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "score_kernel (qsa_score)",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("score_t1984_pos30000"),
+                     "kernel": "score4_kernel (qsa_score)",
                      "algorithmic_bytes_per_launch": by, "scores_per_launch": n_scores,
                      "flops_per_launch": flops, "mean_launch_us": mean_launch_s * 1e6,
                      "launch_timing": "HIP events around %d back-to-back qsa_score calls per "
