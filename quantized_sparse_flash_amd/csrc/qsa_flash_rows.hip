@@ -321,9 +321,9 @@ void flash_rows_staged_kernel(RowArgs a) {
   uint8_t* img = img_all[wave];
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(rows_lds_addr(img));  // wave-uniform
 
-  const int64_t nkv = (int64_t)a.pos0 + t + 1;
-  const bool explicit_ids = nkv > a.budget;
-  const int nsel = explicit_ids ? a.budget : (int)nkv;
+  // only rows above budget come here (the tile kernel attends the rest):
+  // every row selects exactly `budget` cells through its ids
+  const int nsel = a.budget;
   const int nst = (nsel + kStage - 1) / kStage;
 
   const int n = lane & 15, j = lane >> 4;
@@ -375,15 +375,10 @@ void flash_rows_staged_kernel(RowArgs a) {
   const int8_t* vq_g = a.vq + (int64_t)g * a.n_cells * kHeadDim;
   const _Float16* ksc_g = a.ksc + (int64_t)g * a.n_cells * kNBlk;
   const _Float16* vsc_g = a.vsc + (int64_t)g * a.n_cells * kNBlk;
-  const int32_t* ids_row = a.ids + ((int64_t)t * G + g) * a.budget;  // explicit rows only
+  const int32_t* ids_row = a.ids + ((int64_t)t * G + g) * a.budget;
   auto clamp_cell = [&](int c) -> int {
     c = c < 0 ? 0 : c;
     return (int64_t)c >= a.n_cells ? (int)(a.n_cells - 1) : c;
-  };
-  // identity rows: the cell of chunk position `lane` is the position itself
-  auto identity_id = [&](int k) -> int {
-    const int p = k * kChunk + lane;
-    return p < nsel ? p : 0;
   };
 
   // per-lane offsets of a stage's copies, shared by its K and V halves:
@@ -424,8 +419,8 @@ void flash_rows_staged_kernel(RowArgs a) {
     else
       dma4(scales, o[kStage / 4], lds0 + img_scales);
   };
-  // ids of chunk k into the image (explicit rows; positions past the row
-  // read its last id, which the softmax masks)
+  // ids of chunk k into the image (positions past the row read its last
+  // id, which the softmax masks)
   auto issue_ids = [&](int k) {
     const int p = min(k * kChunk + lane, nsel - 1);
     dma4(ids_row, 4 * p, lds0 + kImgIds);
@@ -445,8 +440,8 @@ void flash_rows_staged_kernel(RowArgs a) {
   int cells[kCopiesPerHalf];  // cells of the next stage's copies
   Off offs[kCopiesPerHalf];
   {
-    const int ids0 = explicit_ids ? clamp_cell(ids_row[min(lane, nsel - 1)]) : identity_id(0);
-    ids_next = explicit_ids ? clamp_cell(ids_row[min(kChunk + lane, nsel - 1)]) : identity_id(1);
+    const int ids0 = clamp_cell(ids_row[min(lane, nsel - 1)]);
+    ids_next = clamp_cell(ids_row[min(kChunk + lane, nsel - 1)]);
     // both loads complete before the first copy (the copies' waits count
     // copies only)
     asm volatile("" : : "v"(ids0), "v"(ids_next));
@@ -464,7 +459,7 @@ void flash_rows_staged_kernel(RowArgs a) {
     // ---- K phase: K of stage s into registers, K of stage s + 1 started.
     // Outstanding behind K of stage s: V of stage s, after the ids copy of
     // the previous stage's V phase when there was one.
-    if (!even && explicit_ids)
+    if (!even)
       wait_copies_10();
     else
       wait_copies_9();
@@ -554,11 +549,11 @@ void flash_rows_staged_kernel(RowArgs a) {
     }
     const bool new_chunk = even && k >= 1;  // the ids of chunk k + 1 are due
     int ids_raw = 0;
-    if (new_chunk && explicit_ids) ids_raw = *reinterpret_cast<const int*>(img + kImgIds + 4 * lane);
+    if (new_chunk) ids_raw = *reinterpret_cast<const int*>(img + kImgIds + 4 * lane);
     wait_lds_reads();
-    if (new_chunk) ids_next = explicit_ids ? clamp_cell(ids_raw) : identity_id(k + 1);
+    if (new_chunk) ids_next = clamp_cell(ids_raw);
     if (more) {
-      if (even && explicit_ids) issue_ids(k + 2);
+      if (even) issue_ids(k + 2);
       issue_half(offs, vq_g, vsc_g, kImgV, kImgVs);
       // stage s + 2 lies in chunk k + 1 for either parity of s
       if (s + 2 < nst) cells_of(s + 2, ids_next, cells);
@@ -602,6 +597,8 @@ hipError_t launch_flash_rows(const RowArgs& args_in, bool split, int t_begin,
   if (split) t_begin = 0;
   a.n_items = split ? a.T * a.KC * a.G : (a.T - t_begin) * a.G;
   if (a.n_items <= 0) return hipSuccess;
+  // the fused row kernel attends rows above budget only
+  if (!split && (int64_t)a.pos0 + t_begin + 1 <= a.budget) return hipErrorInvalidValue;
   dim3 grid((a.n_items + 3) / 4), block(256);
   if (!split && kXcds % a.G == 0) {
     // kXcds / G workgroup slots per round serve each group, 4 rows apiece

@@ -31,8 +31,9 @@ hipError_t launch_merge(const float* part, _Float16* out, int T, int H, int pos0
 // scales per row.
 hipError_t launch_quantize(const _Float16* x, int8_t* codes, _Float16* scales, int64_t rows,
                            hipStream_t stream);
-// Row kernel: one wavefront per (token, group) row for tokens [t_begin, T)
-// (fused), or per (token, group, chunk) for all tokens (split mode).
+// Row kernels: one wavefront per (token, group) row for tokens [t_begin, T),
+// all of which must be above budget (fused), or per (token, group, chunk)
+// for all tokens (split mode).
 hipError_t launch_flash_rows(const RowArgs& a, bool split, int t_begin, hipStream_t stream);
 // Tile path: fused attention of tokens [0, t_count), all under budget.
 // launch_tile_prepare dequantises cells [0, pos0 + t_count) of every group
