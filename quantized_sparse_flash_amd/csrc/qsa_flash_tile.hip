@@ -141,22 +141,10 @@ __device__ __forceinline__ void wg_barrier() {
 // Max / sum over the four 16-lane groups of a wave (lanes n, n+16, n+32,
 // n+48), on the VALU: v_permlane16_swap pairs rows {0,1} and {2,3}, then
 // v_permlane32_swap pairs the two halves.
-__device__ __forceinline__ float lane_group_max(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float lane_group_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
+// (the asm swaps of qsa_device.h: the compiler's builtins for these swaps
+// can hand one operation the same result twice)
+__device__ __forceinline__ float lane_group_max(float v) { return wave_max_xor16_32(v); }
+__device__ __forceinline__ float lane_group_sum(float v) { return wave_sum_xor16_32(v); }
 
 // Byte offset of the 16-byte group `grp` (8 dims) of K row `cell`.
 __device__ __forceinline__ int kimg_off(int cell, int grp) {

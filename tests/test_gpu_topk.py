@@ -29,8 +29,12 @@ def test_topk_matches_oracle(T, pos0, budget, kind):
     np.testing.assert_array_equal(gpu_topk(inp), ref)
 
 
-def test_topk_all_equal_and_monotone_rows():
-    T, pos0, B = 4, 3000, 2051
+@pytest.mark.parametrize("T,pos0", [(4, 3000), (3, 20000)])
+def test_topk_all_equal_and_monotone_rows(T, pos0):
+    # at 20,000 cells (the streamed-list kernel) an all-equal row puts every
+    # key at the sampled threshold, more than the list holds: the radix and
+    # bitmap passes then re-read the row from memory
+    B = 2051
     inp = _inputs_with_scores(T, pos0, B, "normal", seed=2)
     N = inp.n_cells
     for s in (np.zeros((T, 2, N), np.float32),
