@@ -293,10 +293,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     issue_copy(img_g + (int64_t)c * kImg + kHalf, lds_addr(kv) + (2 + (c & 1)) * kHalf);
   };
 
-  // the first chunk images stream in while Q loads
+  // K(0) streams in while Q loads; V(0) and K(1) follow once both are in
+  // (below), during chunk 0's scores
   copy_k(0);
-  copy_v(0);
-  if (nch > 1) copy_k(1);
 
   half8_t qf[8];  // Q^T k-step s: dims 32 s + 8 j .. +7
   {
@@ -383,8 +382,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   };
 
   // One pass over the block's chunks; returns true when the fast pass must
-  // be redone exactly (SAFE = false only).  The fast pass finds its first
-  // chunk images (and K of the second) already requested.
+  // be redone exactly (SAFE = false only).  The fast pass finds K(0) in
+  // LDS and V(0), K(1) requested.
   auto run = [&](auto SAFE_T) -> bool {
     constexpr bool SAFE = decltype(SAFE_T)::value;
     f32x4 oacc[16];
@@ -559,8 +558,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       }
       if (c < nch) step(c, P0{});
     } else {
-      wait_vmcnt0();
-      wg_barrier();
       f32x4 s_cur[4];
       scores(std::integral_constant<int, 0>{}, s_cur);
       // two chunks per trip: the score registers trade roles, no copies
@@ -634,12 +631,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     return false;
   };
 
-  // Q is in registers before any copy is issued: a compiler-visible wait, so
-  // that no count-based wait for the Q loads is left inside the loop (it
-  // would also wait for the copies, which the compiler does not count)
+  // Q and every wave's share of K(0) are in before V(0) and K(1) are
+  // requested: a compiler-visible wait, so that no count-based wait for the
+  // Q loads is left inside the loop (it would also wait for the copies,
+  // which the compiler does not count), then a barrier
   if (tid == 0) s_redo = 0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  copy_v(0);
+  if (nch > 1) copy_k(1);
   if (run(std::false_type{})) run(std::true_type{});
 }
 
