@@ -88,3 +88,23 @@ def test_topk_register_rows_with_ties_and_gaps(kind):
         inp.scores = s
     ref = oracle.select(T, pos0, B, inp.scores, 2, inp.n_cells)
     np.testing.assert_array_equal(gpu_topk(inp), ref)
+
+
+@pytest.mark.parametrize("pos0,ept", [(12000, 32), (20000, 64)])
+def test_topk_rows_whose_sample_holds_the_largest_scores(pos0, ept):
+    # The threshold comes from 1024 sampled cells: for s < 16, the 64 cells
+    # from 512 i + 64 (s // 2) on, slice i = s * ept / 16 (512 threads,
+    # ept slices).  Raising exactly those cells far above the rest puts the
+    # sample's rank-r key among them, so fewer than budget cells reach the
+    # threshold: the select must fall back (register passes for rows of at
+    # most 16,384 cells, passes that re-read the row above) and still give
+    # the oracle's ids
+    T, B = 3, 2051
+    inp = _inputs_with_scores(T, pos0, B, "normal", seed=pos0 + 5)
+    s = inp.scores
+    for k in range(16):
+        c0 = 512 * (k * ept // 16) + 64 * (k // 2)
+        s[:, :, c0:c0 + 64] += np.float32(100.0)
+    inp.scores = s
+    ref = oracle.select(T, pos0, B, inp.scores, 2, inp.n_cells)
+    np.testing.assert_array_equal(gpu_topk(inp), ref)
