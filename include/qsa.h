@@ -168,12 +168,13 @@ int qsa_flash(const qsa_shape *shape, const _Float16 *q, const int8_t *kq, const
  * then attends.  qsa_flash_prepare enqueues the first half only (nothing
  * when no token is under budget); qsa_flash_attend enqueues the second
  * half and reads the workspace that a qsa_flash_prepare call with the same
- * shape and K/V arguments filled earlier on the same stream (or one ordered
- * before it).  The pair computes exactly what one fused qsa_flash call
- * computes, and qsa_flash (fused mode) is these two calls.  Arguments,
- * alignment and error behaviour are those of qsa_flash; `out` is written by
- * qsa_flash_attend.  Attending without a prepared workspace gives
- * unspecified output values (never an out-of-bounds access).
+ * shape, K/V arguments and workspace_bytes filled earlier on the same stream
+ * (or one ordered before it); qsa_flash_attend may run more than once on
+ * one prepared workspace.  The pair computes exactly what one fused
+ * qsa_flash call computes, and qsa_flash (fused mode) is these two calls.
+ * Arguments, alignment and error behaviour are those of qsa_flash; `out` is
+ * written by qsa_flash_attend.  Attending without a prepared workspace
+ * gives unspecified output values (never an out-of-bounds access).
  */
 int qsa_flash_prepare(const qsa_shape *shape, const int8_t *kq, const _Float16 *ksc,
                       const int8_t *vq, const _Float16 *vsc, void *workspace,
@@ -189,7 +190,14 @@ int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq
  * helper.  The fused path dequantises the cells that tokens under budget
  * share -- cells [0, pos0 + t_id) of every group, t_id being the number of
  * such tokens -- once per call into this workspace: 64 KB per group and
- * 64-cell chunk (fp16 K and V^T).
+ * 64-cell chunk (fp16 K and V^T).  When the tiled attention of those tokens
+ * leaves compute units idle and has blocks of at least 12 chunks (a few
+ * tokens after a long prefix), those blocks of 64 queries run as 2 or 3
+ * workgroups over consecutive ranges of their chunks that merge their
+ * partial results through the workspace; it then also holds, per split
+ * block, one partial of 64 x 258 floats per piece and a 4-byte counter
+ * (the counters rounded up to 256 bytes).  qsa_flash_prepare clears the
+ * counters; every call leaves them at zero.
  */
 int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
 
@@ -206,11 +214,14 @@ int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
  * in time on the same GPU (other streams, other threads) race and give
  * unspecified output; calls ordered on one stream are fine.  Nothing in the
  * array needs to start at zero (each call writes every byte it reads).
- *   returns QSA_ERR_TOO_LARGE when qsa_flash_workspace_bytes(shape) exceeds
- *   QSA_NOALLOC_SCRATCH_BYTES (e.g. more than 256 KV-group x 64-cell
- *   chunks of identity prefix: 2 groups up to budget 8192), checked before
- *   anything else touches the device; QSA_ERR_DEVICE when the device or
- *   the array's address cannot be queried.
+ *   returns QSA_ERR_TOO_LARGE when the fused path's chunk images (64 KB
+ *   per KV group and 64-cell chunk of identity prefix) exceed
+ *   QSA_NOALLOC_SCRATCH_BYTES (more than 256 of them, e.g. 2 groups past
+ *   an 8192-cell prefix), checked before anything else touches the device;
+ *   QSA_ERR_DEVICE when the device or the array's address cannot be
+ *   queried.  The scratch beyond the images holds the split pieces that
+ *   qsa_flash_workspace_bytes makes room for, as far as it reaches; blocks
+ *   it cannot hold run whole, which changes the output only by rounding.
  */
 int qsa_flash_noalloc(const qsa_shape *shape, const _Float16 *q, const int8_t *kq,
                       const _Float16 *ksc, const int8_t *vq, const _Float16 *vsc,

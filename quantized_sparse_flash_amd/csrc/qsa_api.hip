@@ -131,9 +131,17 @@ int flash_args(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _F
   return QSA_OK;
 }
 
-// The fused path's workspace: needed for the identity prefix only.
-int check_workspace(const qsa_shape* s, const void* workspace, int64_t workspace_bytes) {
-  const int64_t need = qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+// The fused path's workspace (needed for the identity prefix only): the
+// public calls ask for qsa_flash_workspace_bytes, which includes room for
+// the split pieces of a tiled grid that leaves CUs idle; qsa_flash_noalloc
+// asks only for the chunk images and splits as far as its scratch holds.
+int64_t full_workspace(const qsa_shape* s) {
+  return qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+}
+int64_t min_workspace(const qsa_shape* s) {
+  return qsa::tile_workspace_min_bytes(s->n_groups, identity_tokens(s), s->pos0);
+}
+int check_workspace(const void* workspace, int64_t workspace_bytes, int64_t need) {
   if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need))
     return QSA_ERR_ARG;
   return QSA_OK;
@@ -147,43 +155,39 @@ int check_attend(const qsa_shape* s, const _Float16* q, const int32_t* ids, cons
   return QSA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int qsa_flash_prepare(const qsa_shape* s, const int8_t* kq, const _Float16* ksc,
-                      const int8_t* vq, const _Float16* vsc, void* workspace,
-                      int64_t workspace_bytes, void* stream) {
+int prepare_impl(const qsa_shape* s, const int8_t* kq, const _Float16* ksc, const int8_t* vq,
+                 const _Float16* vsc, void* workspace, int64_t workspace_bytes, void* stream,
+                 int64_t need) {
   qsa::RowArgs a;
   int rc = flash_args(s, nullptr, kq, ksc, vq, vsc, nullptr, nullptr, nullptr, &a);
-  if (rc == QSA_OK) rc = check_workspace(s, workspace, workspace_bytes);
+  if (rc == QSA_OK) rc = check_workspace(workspace, workspace_bytes, need);
   if (rc != QSA_OK) return rc;
-  return launch_status(
-      qsa::launch_tile_prepare(a, identity_tokens(s), workspace, (hipStream_t)stream));
+  return launch_status(qsa::launch_tile_prepare(a, identity_tokens(s), workspace,
+                                                workspace_bytes, (hipStream_t)stream));
 }
 
-int qsa_flash_attend(const qsa_shape* s, const _Float16* q, const int8_t* kq,
-                     const _Float16* ksc, const int8_t* vq, const _Float16* vsc,
-                     const int32_t* ids, _Float16* out, void* workspace, int64_t workspace_bytes,
-                     void* stream) {
+int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
+                const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+                void* workspace, int64_t workspace_bytes, void* stream, int64_t need) {
   qsa::RowArgs a;
   int rc = flash_args(s, q, kq, ksc, vq, vsc, ids, out, nullptr, &a);
   if (rc == QSA_OK) rc = check_attend(s, q, ids, out);
-  if (rc == QSA_OK) rc = check_workspace(s, workspace, workspace_bytes);
+  if (rc == QSA_OK) rc = check_workspace(workspace, workspace_bytes, need);
   if (rc != QSA_OK) return rc;
   // tokens under budget (a prefix of the chunk) see a common prefix of
   // cells, dequantised once into the workspace and shared by the tiled
   // kernel; tokens above budget gather their own ids row by row
   const int t_id = identity_tokens(s);
   hipStream_t st = (hipStream_t)stream;
-  rc = launch_status(qsa::launch_tile_attend(a, t_id, workspace, st));
+  rc = launch_status(qsa::launch_tile_attend(a, t_id, workspace, workspace_bytes, st));
   if (rc != QSA_OK) return rc;
   return launch_status(qsa::launch_flash_rows(a, false, t_id, st));
 }
 
-int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
-              const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
-              float* part, void* workspace, int64_t workspace_bytes, void* stream) {
+int flash_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
+               const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+               float* part, void* workspace, int64_t workspace_bytes, void* stream,
+               int64_t need) {
   qsa::RowArgs a;
   int rc = flash_args(s, q, kq, ksc, vq, vsc, ids, out, part, &a);
   if (rc != QSA_OK) return rc;
@@ -193,11 +197,42 @@ int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Fl
     return launch_status(qsa::launch_flash_rows(a, true, 0, (hipStream_t)stream));
   }
   rc = check_attend(s, q, ids, out);
-  if (rc == QSA_OK) rc = check_workspace(s, workspace, workspace_bytes);
+  if (rc == QSA_OK) rc = check_workspace(workspace, workspace_bytes, need);
   if (rc != QSA_OK) return rc;
-  rc = qsa_flash_prepare(s, kq, ksc, vq, vsc, workspace, workspace_bytes, stream);
+  rc = prepare_impl(s, kq, ksc, vq, vsc, workspace, workspace_bytes, stream, need);
   if (rc != QSA_OK) return rc;
-  return qsa_flash_attend(s, q, kq, ksc, vq, vsc, ids, out, workspace, workspace_bytes, stream);
+  return attend_impl(s, q, kq, ksc, vq, vsc, ids, out, workspace, workspace_bytes, stream, need);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_flash_prepare(const qsa_shape* s, const int8_t* kq, const _Float16* ksc,
+                      const int8_t* vq, const _Float16* vsc, void* workspace,
+                      int64_t workspace_bytes, void* stream) {
+  const int rc = check_shape(s);
+  if (rc != QSA_OK) return rc;
+  return prepare_impl(s, kq, ksc, vq, vsc, workspace, workspace_bytes, stream, full_workspace(s));
+}
+
+int qsa_flash_attend(const qsa_shape* s, const _Float16* q, const int8_t* kq,
+                     const _Float16* ksc, const int8_t* vq, const _Float16* vsc,
+                     const int32_t* ids, _Float16* out, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  const int rc = check_shape(s);
+  if (rc != QSA_OK) return rc;
+  return attend_impl(s, q, kq, ksc, vq, vsc, ids, out, workspace, workspace_bytes, stream,
+                     full_workspace(s));
+}
+
+int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
+              const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+              float* part, void* workspace, int64_t workspace_bytes, void* stream) {
+  const int rc = check_shape(s);
+  if (rc != QSA_OK) return rc;
+  return flash_impl(s, q, kq, ksc, vq, vsc, ids, out, part, workspace, workspace_bytes, stream,
+                    part ? 0 : full_workspace(s));
 }
 
 int qsa_merge(const qsa_shape* s, const float* part, _Float16* out, void* stream) {
@@ -259,16 +294,15 @@ int qsa_flash_noalloc(const qsa_shape* s, const _Float16* q, const int8_t* kq,
     rc = check_attend(s, q, ids, out);
     if (rc != QSA_OK) return rc;
   }
-  const int64_t need =
-      part ? 0 : qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+  const int64_t need = part ? 0 : min_workspace(s);
   if (need > QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_TOO_LARGE;
   void* ws = nullptr;
   if (need > 0) {
     ws = scratch_ptr();
     if (!ws) return QSA_ERR_DEVICE;
   }
-  return qsa_flash(s, q, kq, ksc, vq, vsc, ids, out, part, ws,
-                   need > 0 ? (int64_t)QSA_NOALLOC_SCRATCH_BYTES : 0, stream);
+  return flash_impl(s, q, kq, ksc, vq, vsc, ids, out, part, ws,
+                    need > 0 ? (int64_t)QSA_NOALLOC_SCRATCH_BYTES : 0, stream, need);
 }
 
 }  // extern "C"

@@ -87,6 +87,14 @@ __host__ __device__ constexpr int tile_queries(int waves) { return kQpw * waves;
 __host__ __device__ inline int tile_blocks(int t_count, int waves) {
   return (t_count * kHpg + tile_queries(waves) - 1) / tile_queries(waves);
 }
+// Chunks block b attends: the cells its last token sees, in 64-cell chunks.
+__host__ __device__ inline int block_chunks(int b, int t_count, int pos0, int waves) {
+  const int q_last = min((b + 1) * tile_queries(waves), t_count * kHpg) - 1;
+  return (pos0 + q_last / kHpg + 1 + kChunk - 1) / kChunk;
+}
+// First chunk of piece p of a block of nch chunks split into k pieces.
+__host__ __device__ constexpr int piece_start(int nch, int p, int k) { return p * nch / k; }
+constexpr int kMaxPieces = 3;  // pieces per split block
 // MI355X compute units: below this many 8-wave workgroups the grid would
 // leave CUs idle, and 4-wave workgroups of half as many tokens are used.
 constexpr int kCus = 256;
@@ -94,6 +102,20 @@ constexpr float kP16Max = 65504.0f;         // largest finite fp16
 constexpr int kHalf = kChunk * kHeadDim * 2;  // bytes of one K or V^T image (32 KB)
 constexpr int kImg = 2 * kHalf;               // bytes per (group, chunk) in the workspace
 constexpr int kHalfCells = kChunk / 2;           // cells per PV k-step
+// A split piece's partial result in the workspace: its O (unnormalised,
+// fp32, one 16-byte group per (wave, M-tile, lane) in that order, as the
+// registers hold it), then (m, l) per query slot.
+__host__ __device__ constexpr int part_floats(int waves) {
+  return tile_queries(waves) * kHeadDim + 2 * tile_queries(waves);
+}
+
+// Where a launch's split pieces keep their counters and partials.
+struct TileSplit {
+  int n_split;  // blocks split per group: the longest ones
+  int pieces;   // workgroups per split block (2 .. kMaxPieces)
+  int* cnt;     // [G * n_split] arrival counters, zero between launches
+  float* part;  // [G * n_split][pieces][part_floats(waves)]
+};
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) const half8_t lds_half8_t;
@@ -174,8 +196,12 @@ __host__ __device__ constexpr int vslot_cell(int j, int e) {
 // CUs than four-wave workgroups do (~1% shorter steps at T=1024); the grid
 // is padded to whole groups of 32 workgroups, and the spare ones return.
 __global__ __launch_bounds__(64) void dequant_chunks_kernel(RowArgs a, int n_needed,
-                                                             int nchunks, uint8_t* ws) {
+                                                             int nchunks, uint8_t* ws, int* cnt,
+                                                             int n_cnt) {
   const int lane = threadIdx.x & 63;
+  // the attention launch's arrival counters start at zero
+  if (blockIdx.x == 0)
+    for (int i = lane; i < n_cnt; i += 64) cnt[i] = 0;
   // workgroups are dealt to the 8 XCDs round robin: the four waves j of one
   // (group, chunk, kk) get indices 8 apart, so they share an XCD's L2 and
   // their pieces of each V^T row merge there into whole lines
@@ -235,38 +261,62 @@ __global__ __launch_bounds__(64) void dequant_chunks_kernel(RowArgs a, int n_nee
 }
 
 // ---------------------------------------------------------------- attention
-template <int kWaves>
+// kSplit: the launch runs split blocks (sp); without it the chunk ranges
+// are the whole blocks at compile time.
+template <int kWaves, bool kSplit>
 __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, int t_count,
                                                                     int nchunks,
-                                                                    const uint8_t* ws) {
+                                                                    const uint8_t* ws,
+                                                                    TileSplit sp) {
   constexpr int kQpb = tile_queries(kWaves);
   constexpr int kCopyOps = kHalf / 1024 / kWaves;  // 1 KB copies per wave per image
-  // K(c) lives in kv[c & 1], V^T(c) in kv[2 + (c & 1)]
+  // K(c) lives in kv[(c - cb) & 1], V^T(c) in kv[2 + ((c - cb) & 1)]
   __shared__ __attribute__((aligned(16))) uint8_t kv[4 * kHalf];
   __shared__ int s_redo;  // set when the fast pass must be redone exactly
+  __shared__ int s_flag;  // a split piece's arrival count
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.G, H = G * kHpg;
   const int n_blocks = tile_blocks(t_count, kWaves);
-  // longest blocks first; consecutive workgroups alternate KV groups
-  const int g = blockIdx.x % G;
-  const int blk = n_blocks - 1 - blockIdx.x / G;
+  // Longest blocks first; consecutive workgroups alternate KV groups.  The
+  // n_split longest blocks of each group come first, each as sp.pieces
+  // pieces over consecutive ranges of its chunks, G workgroups apart, that
+  // merge their partial results; then the other blocks, one workgroup each.
+  int g, blk, sb = -1, piece = 0;
+  if (kSplit && blockIdx.x < sp.pieces * sp.n_split * G) {
+    g = blockIdx.x % G;
+    piece = (blockIdx.x / G) % sp.pieces;
+    const int r = blockIdx.x / (sp.pieces * G);
+    blk = n_blocks - 1 - r;
+    sb = r * G + g;  // split block index: its counter and partial slots
+  } else {
+    const int n_first = kSplit ? sp.pieces * sp.n_split * G : 0;
+    const int i = blockIdx.x - n_first;
+    g = i % G;
+    blk = n_blocks - 1 - (kSplit ? sp.n_split : 0) - i / G;
+  }
   const int q0 = blk * kQpb;                                 // first query of the block
   const int q_last = min(q0 + kQpb, t_count * kHpg) - 1;     // last one
   const int t0 = q0 / kHpg;
-  const int t_last = q_last / kHpg;
   const int nkv_min = a.pos0 + t0 + 1;  // cells every token of the block sees
-  const int nkv_max = a.pos0 + t_last + 1;
-  const int nch = (nkv_max + kChunk - 1) / kChunk;
+  const int nch = block_chunks(blk, t_count, a.pos0, kWaves);
+  // this workgroup's chunks [cb, ce).  The host splits only blocks whose
+  // tokens all see a cell of every piece's first chunk (64 cb < nkv_min),
+  // so each piece's first chunk gives every query a finite softmax
+  // reference.
+  const int cb = (kSplit && sb >= 0) ? piece_start(nch, piece, sp.pieces) : 0;
+  const int ce = (kSplit && sb >= 0) ? piece_start(nch, piece + 1, sp.pieces) : nch;
   const uint8_t* img_g = ws + (int64_t)g * nchunks * kImg;
 
   const int n = lane & 15, j = lane >> 4;
 
-  // ---- this lane's query: slot kQpw w + n of the workgroup
+  // ---- this lane's query: slot kQpw w + n of the workgroup.  Slots past
+  // the last query (a group's last block) compute as if they were its
+  // first token and are never written.
   const int qs = q0 + kQpw * w + n;
   const bool qvalid = qs <= q_last;
   const int qt = qs / kHpg;
   const int qh = g * kHpg + qs % kHpg;
-  const int nkv_q = qvalid ? a.pos0 + qt + 1 : 1;
+  const int nkv_q = qvalid ? a.pos0 + qt + 1 : nkv_min;
   // ---- LDS read addresses of this lane's operand fragments
   // K: row (cell) 16 mt + n, group 4 s + j; s = 4 v + u -> the XOR touches
   // the low 4 bits only, so v and mt are immediates
@@ -288,14 +338,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
 #pragma unroll
     for (int i = 0; i < kCopyOps; ++i) copy16_to_lds(src, copy_voff[i], d + 1024 * i);
   };
-  auto copy_k = [&](int c) { issue_copy(img_g + (int64_t)c * kImg, lds_addr(kv) + (c & 1) * kHalf); };
+  auto copy_k = [&](int c) {
+    issue_copy(img_g + (int64_t)c * kImg, lds_addr(kv) + ((c - cb) & 1) * kHalf);
+  };
   auto copy_v = [&](int c) {
-    issue_copy(img_g + (int64_t)c * kImg + kHalf, lds_addr(kv) + (2 + (c & 1)) * kHalf);
+    issue_copy(img_g + (int64_t)c * kImg + kHalf, lds_addr(kv) + (2 + ((c - cb) & 1)) * kHalf);
   };
 
-  // K(0) streams in while Q loads; V(0) and K(1) follow once both are in
-  // (below), during chunk 0's scores
-  copy_k(0);
+  // K(cb) streams in while Q loads; V(cb) and K(cb + 1) follow once both
+  // are in (below), during the first chunk's scores
+  copy_k(cb);
 
   half8_t qf[8];  // Q^T k-step s: dims 32 s + 8 j .. +7
   {
@@ -382,8 +434,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   };
 
   // One pass over the block's chunks; returns true when the fast pass must
-  // be redone exactly (SAFE = false only).  The fast pass finds K(0) in
-  // LDS and V(0), K(1) requested.
+  // be redone exactly (SAFE = false only).  The fast pass finds K(cb) in
+  // LDS and V(cb), K(cb + 1) requested.
   auto run = [&](auto SAFE_T) -> bool {
     constexpr bool SAFE = decltype(SAFE_T)::value;
     f32x4 oacc[16];
@@ -398,7 +450,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       constexpr int P = decltype(P_T)::value;
       wait_vmcnt0();  // this wave's copies of K(c) and V(c) have landed
       wg_barrier();   // ... every wave's; and nobody reads chunk c - 1 any more
-      if (c + 1 < nch) {
+      if (c + 1 < ce) {
         copy_k(c + 1);
         copy_v(c + 1);
       }
@@ -431,7 +483,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
       constexpr int kS = 8;            // score stages (k-steps of chunk c + 1)
       constexpr int kStages = kS + 8;  // then PV stages: k-step t / 4, m-tiles 4 (t % 4) ..
       constexpr int kAhead = 1;        // stages whose fragments are read ahead
-      const uint32_t kpar = ((c + 1) & 1) * kHalf, vpar = (c & 1) * kHalf;
+      const uint32_t kpar = ((c + 1 - cb) & 1) * kHalf, vpar = ((c - cb) & 1) * kHalf;
       wait_vmcnt0();  // this wave's copies of K(c+1) and V(c) have landed
       wg_barrier();   // ... every wave's; and nobody reads K(c) or V(c-1) any more
       mask(c, s_cur);
@@ -462,8 +514,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
         for (int mt = 0; mt < 4; ++mt) s_nxt[mt] = zero4();
       }
       static_for<kAhead>([&](auto I) { load(I, fr[decltype(I)::value]); });
-      // chunk 0 always holds cell 0: the reference is finite
-      if (c == 0) m_ref = chunk_max(s_cur);
+      // the workgroup's first chunk holds a visible cell of every query:
+      // the reference is finite
+      if (c == cb) m_ref = chunk_max(s_cur);
       const float nm = -m_ref;
       half8_t pb[2];  // P in B-operand slot order: k-step kk, slot e
       // exponentials of slots 2 i and 2 i + 1 (slot q = 8 kk + e), rounded
@@ -489,19 +542,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
         // 1 and 3, V after 5 and 7.
         if constexpr (kWaves == 8) {
           if constexpr (i == 2) {
-            if (c + 2 < nch) copy_k(c + 2);
+            if (c + 2 < ce) copy_k(c + 2);
           }
           if constexpr (i == 6) {
-            if (c + 1 < nch) copy_v(c + 1);
+            if (c + 1 < ce) copy_v(c + 1);
           }
         } else if constexpr (i == 1 || i == 3 || i == 5 || i == 7) {
           constexpr int h = (i == 1 || i == 5) ? 0 : 1;  // first or second half
           constexpr bool isk = i < 4;
           const int cc = isk ? c + 2 : c + 1;
-          if (cc < nch) {
+          if (cc < ce) {
             const uint8_t* src = img_g + (int64_t)cc * kImg + (isk ? 0 : kHalf);
             const uint32_t dst =
-                lds_addr(kv) + ((isk ? 0 : 2) + (cc & 1)) * kHalf + w * (kHalf / kWaves);
+                lds_addr(kv) + ((isk ? 0 : 2) + ((cc - cb) & 1)) * kHalf + w * (kHalf / kWaves);
 #pragma unroll
             for (int op = (kCopyOps / 2) * h; op < (kCopyOps / 2) * (h + 1); ++op)
               copy16_to_lds(src, copy_voff[op], dst + 1024 * op);
@@ -549,25 +602,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     if constexpr (SAFE) {
-      copy_k(0);
-      copy_v(0);
-      int c = 0;
-      for (; c + 1 < nch; c += 2) {
+      copy_k(cb);
+      copy_v(cb);
+      int c = cb;
+      for (; c + 1 < ce; c += 2) {
         step(c, P0{});
         step(c + 1, P1{});
       }
-      if (c < nch) step(c, P0{});
+      if (c < ce) step(c, P0{});
     } else {
       f32x4 s_cur[4];
       scores(std::integral_constant<int, 0>{}, s_cur);
       // two chunks per trip: the score registers trade roles, no copies
       f32x4 s_alt[4];
-      int c = 0;
-      for (; c + 2 < nch; c += 2) {
+      int c = cb;
+      for (; c + 2 < ce; c += 2) {
         step_fast(c, s_cur, s_alt, F_{});
         step_fast(c + 1, s_alt, s_cur, F_{});
       }
-      if (c + 1 < nch) {
+      if (c + 1 < ce) {
         step_fast(c, s_cur, s_alt, F_{});
         step_fast(c + 1, s_alt, s_cur, T_{});
       } else {
@@ -576,15 +629,92 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
     }
 
     // ---- finalise: O / l -> fp16; lane (n, j) holds dims 16 mt + 4 j + i
-    const float l_tot = lane_group_sum(l_run);
+    float l_tot = lane_group_sum(l_run);
     if constexpr (!SAFE) {
       // workgroup vote: every P value is below l, so l < 65504 means no P
-      // overflowed fp16; otherwise (scores far above the chunk-0 reference)
-      // the block is redone exactly
+      // overflowed fp16; otherwise (scores far above the reference of the
+      // workgroup's first chunk) its chunks are redone exactly
       over = qvalid && !(l_tot < kP16Max);
       if (__builtin_amdgcn_ballot_w64(over) != 0ull) s_redo = 1;
       __syncthreads();
       if (s_redo) return true;
+    }
+
+    // ---- a split block's pieces: each publishes its partial (O, m, l) and
+    // counts itself; the one counted last merges every piece's partial and
+    // writes the block.  Partials travel with write-through stores and loads
+    // that read past this XCD's L2 (cache policy sc1: agent scope), so no
+    // cache write-back or invalidation is needed around the count: a
+    // piece's stores complete (vmcnt) before a barrier, then one relaxed
+    // agent-scope add.  No piece ever waits for another.  The merge runs in
+    // piece order whichever piece merges, so the result does not depend on
+    // the order of arrival.
+    if constexpr (kSplit) {
+      if (sb >= 0) {
+        constexpr int kSc1 = 16;  // cache policy bit sc1
+        constexpr int kPart = part_floats(kWaves);
+        const int np = sp.pieces;
+        auto rsrc = [&](int p) {
+          return __builtin_amdgcn_make_buffer_rsrc(sp.part + ((int64_t)sb * np + p) * kPart,
+                                                   (short)0, 4 * kPart, kBufferFlags);
+        };
+        const auto rs_own = rsrc(piece);
+        const int o_off = w * (16 * 64 * 16) + 16 * lane;  // + 1024 mt: (w, mt, lane) group
+        const int ml_off = (kQpb * kHeadDim + 2 * (kQpw * w + n)) * 4;
+        int* cntp = sp.cnt + sb;
+#pragma unroll
+        for (int mt = 0; mt < 16; ++mt)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oacc[mt]), rs_own,
+                                                 o_off + 1024 * mt, 0, kSc1);
+        if (j == 0) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref), rs_own, ml_off, 0, kSc1);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot), rs_own, ml_off + 4, 0,
+                                                kSc1);
+        }
+        wait_vmcnt0();    // this thread's partial has reached memory ...
+        __syncthreads();  // ... and every thread's, before the count
+        if (tid == 0)
+          s_flag = __hip_atomic_fetch_add(cntp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (s_flag != np - 1) return false;  // a piece counted later merges
+        // every other piece's partial is complete: log-sum-exp merge in
+        // piece order, this piece's from its registers
+        float mp[kMaxPieces], lp[kMaxPieces], mm = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < kMaxPieces; ++p) {
+          if (p < np) {
+            const auto rs = rsrc(p);
+            mp[p] = p == piece ? m_ref
+                               : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ml_off, 0, kSc1));
+            lp[p] = p == piece ? l_tot
+                               : __uint_as_float(
+                                     __builtin_amdgcn_raw_buffer_load_b32(rs, ml_off + 4, 0, kSc1));
+            mm = fmaxf(mm, mp[p]);
+          }
+        }
+        f32x4 acc[16];
+        float lsum = 0.f;
+#pragma unroll
+        for (int p = 0; p < kMaxPieces; ++p) {
+          if (p < np) {
+            const float wp = fast_exp2(mp[p] - mm);
+            lsum = p == 0 ? wp * lp[p] : lsum + wp * lp[p];
+            const auto rs = rsrc(p);
+#pragma unroll
+            for (int mt = 0; mt < 16; ++mt) {
+              const f32x4 op =
+                  p == piece ? oacc[mt]
+                             : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             rs, o_off + 1024 * mt, 0, kSc1));
+              acc[mt] = p == 0 ? wp * op : acc[mt] + wp * op;
+            }
+          }
+        }
+        l_tot = lsum;
+#pragma unroll
+        for (int mt = 0; mt < 16; ++mt) oacc[mt] = acc[mt];
+        if (tid == 0) __hip_atomic_store(cntp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
 
     if constexpr (SAFE) {
@@ -638,40 +768,128 @@ __global__ __launch_bounds__(kWaves * 64, 1) void flash_tile_kernel(RowArgs a, i
   if (tid == 0) s_redo = 0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  copy_v(0);
-  if (nch > 1) copy_k(1);
+  copy_v(cb);
+  if (cb + 1 < ce) copy_k(cb + 1);
   if (run(std::false_type{})) run(std::true_type{});
 }
 
-int64_t tile_workspace_bytes(int G, int t_count, int pos0) {
+namespace {
+
+// Bytes of the dequantised chunk images: cells [0, pos0 + t_count) of every
+// group, 64 KB per (group, 64-cell chunk).
+int64_t tile_image_bytes(int G, int t_count, int pos0) {
   if (t_count <= 0) return 0;
   const int64_t n_needed = (int64_t)pos0 + t_count;  // cells the last identity token sees
   const int64_t nchunks = (n_needed + kChunk - 1) / kChunk;
   return (int64_t)G * nchunks * kImg;
 }
+// Bytes of the split pieces' counters (256-byte rounded) and partials on
+// the 4-wave grid.
+int64_t split_bytes(int G, int n_split, int pieces) {
+  if (n_split <= 0) return 0;
+  const int64_t n = (int64_t)G * n_split;
+  return (n * 4 + 255) / 256 * 256 + pieces * n * (int64_t)part_floats(4) * 4;
+}
 
-hipError_t launch_tile_prepare(const RowArgs& a, int t_count, void* ws, hipStream_t stream) {
+// Which blocks of a launch run as several pieces.  Only a 4-wave grid that
+// leaves CUs idle splits, and only into those idle CUs, so every workgroup
+// still starts in the launch's first round (a second round starts late on
+// this hardware).  A piece's publish, count and the last piece's merge cost
+// about three chunk times, so only blocks of at least 12 chunks (and 3/4
+// of the longest block's) are split: the long blocks of a few tokens after
+// a long prefix.  They get as many pieces (up to 3, each at least 6
+// chunks) as the idle CUs allow for all of them; when even 2 pieces each do
+// not fit, nothing is split (an unsplit long block would still set the
+// launch's length).
+struct SplitPlan {
+  int n_split = 0, pieces = 1;
+};
+SplitPlan split_plan(int G, int t_count, int pos0) {
+  SplitPlan sp;
+  if (t_count <= 0 || tile_blocks(t_count, 8) * G >= kCus) return sp;
+  const int nb = tile_blocks(t_count, 4);
+  const int idle = kCus - nb * G;
+  const int top = block_chunks(nb - 1, t_count, pos0, 4);
+  if (idle < G || top < 12) return sp;
+  const int lim = max(12, (3 * top + 3) / 4);
+  int count = 0;
+  while (count < nb && block_chunks(nb - 1 - count, t_count, pos0, 4) >= lim) ++count;
+  // every token of a split block must see a cell of each piece's first
+  // chunk: 64 cb < pos0 + t0 + 1 for the block's first token t0
+  auto fits = [&](int s, int k) {
+    for (int b = nb - s; b < nb; ++b) {
+      const int nch = block_chunks(b, t_count, pos0, 4);
+      const int64_t t0 = (int64_t)b * tile_queries(4) / kHpg;
+      if ((int64_t)kChunk * piece_start(nch, k - 1, k) >= pos0 + t0 + 1) return false;
+    }
+    return true;
+  };
+  for (int k = kMaxPieces; k >= 2; --k) {
+    if (lim >= 6 * k && count * (k - 1) * G <= idle && fits(count, k)) {
+      sp.n_split = count;
+      sp.pieces = k;
+      return sp;
+    }
+  }
+  return sp;
+}
+// The plan and its pointers, or no split when ws_bytes does not hold the
+// plan's pieces beyond the images (a part of the plan would leave long
+// blocks whole, and they would still set the launch's length).
+TileSplit split_args(int G, int t_count, int pos0, void* ws, int64_t ws_bytes) {
+  const SplitPlan plan = split_plan(G, t_count, pos0);
+  const int64_t room = ws_bytes - tile_image_bytes(G, t_count, pos0);
+  const int s = split_bytes(G, plan.n_split, plan.pieces) <= room ? plan.n_split : 0;
+  TileSplit sp{s, s > 0 ? plan.pieces : 1, nullptr, nullptr};
+  if (s > 0) {
+    uint8_t* base = static_cast<uint8_t*>(ws) + tile_image_bytes(G, t_count, pos0);
+    const int64_t n = (int64_t)G * s;
+    sp.cnt = reinterpret_cast<int*>(base);
+    sp.part = reinterpret_cast<float*>(base + (n * 4 + 255) / 256 * 256);
+  }
+  return sp;
+}
+
+}  // namespace
+
+int64_t tile_workspace_min_bytes(int G, int t_count, int pos0) {
+  return tile_image_bytes(G, t_count, pos0);
+}
+
+int64_t tile_workspace_bytes(int G, int t_count, int pos0) {
+  const SplitPlan plan = split_plan(G, t_count, pos0);
+  return tile_image_bytes(G, t_count, pos0) + split_bytes(G, plan.n_split, plan.pieces);
+}
+
+hipError_t launch_tile_prepare(const RowArgs& a, int t_count, void* ws, int64_t ws_bytes,
+                               hipStream_t stream) {
   if (t_count <= 0) return hipSuccess;
   const int n_needed = a.pos0 + t_count;
   const int nchunks = (n_needed + kChunk - 1) / kChunk;
+  const TileSplit sp = split_args(a.G, t_count, a.pos0, ws, ws_bytes);
   dequant_chunks_kernel<<<dim3((2 * a.G * nchunks + 7) / 8 * 32), dim3(64), 0, stream>>>(
-      a, n_needed, nchunks, static_cast<uint8_t*>(ws));
+      a, n_needed, nchunks, static_cast<uint8_t*>(ws), sp.cnt, a.G * sp.n_split);
   return hipGetLastError();
 }
 
-hipError_t launch_tile_attend(const RowArgs& a, int t_count, const void* ws, hipStream_t stream) {
+hipError_t launch_tile_attend(const RowArgs& a, int t_count, void* ws, int64_t ws_bytes,
+                              hipStream_t stream) {
   if (t_count <= 0) return hipSuccess;
   const int n_needed = a.pos0 + t_count;
   const int nchunks = (n_needed + kChunk - 1) / kChunk;
   const uint8_t* img = static_cast<const uint8_t*>(ws);
   const int blocks8 = tile_blocks(t_count, 8);
   if (blocks8 * a.G >= kCus) {
-    flash_tile_kernel<8><<<dim3(blocks8 * a.G), dim3(8 * 64), 0, stream>>>(a, t_count, nchunks,
-                                                                             img);
+    flash_tile_kernel<8, false><<<dim3(blocks8 * a.G), dim3(8 * 64), 0, stream>>>(
+        a, t_count, nchunks, img, TileSplit{0, 1, nullptr, nullptr});
   } else {
     const int blocks4 = tile_blocks(t_count, 4);
-    flash_tile_kernel<4><<<dim3(blocks4 * a.G), dim3(4 * 64), 0, stream>>>(a, t_count, nchunks,
-                                                                             img);
+    const TileSplit sp = split_args(a.G, t_count, a.pos0, ws, ws_bytes);
+    const dim3 grid((blocks4 + (sp.pieces - 1) * sp.n_split) * a.G);
+    if (sp.n_split > 0)
+      flash_tile_kernel<4, true><<<grid, dim3(4 * 64), 0, stream>>>(a, t_count, nchunks, img, sp);
+    else
+      flash_tile_kernel<4, false><<<grid, dim3(4 * 64), 0, stream>>>(a, t_count, nchunks, img, sp);
   }
   return hipGetLastError();
 }

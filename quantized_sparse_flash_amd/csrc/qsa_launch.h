@@ -37,10 +37,15 @@ hipError_t launch_quantize(const _Float16* x, int8_t* codes, _Float16* scales, i
 hipError_t launch_flash_rows(const RowArgs& a, bool split, int t_begin, hipStream_t stream);
 // Tile path: fused attention of tokens [0, t_count), all under budget.
 // launch_tile_prepare dequantises cells [0, pos0 + t_count) of every group
-// into `ws` (which must hold tile_workspace_bytes(G, t_count, pos0) bytes);
-// launch_tile_attend then attends from it.
+// into `ws` (ws_bytes bytes, at least tile_workspace_min_bytes) and clears
+// the split pieces' counters; launch_tile_attend then attends from it.
+// Both take the same ws_bytes: it decides how many of the longest blocks
+// run as two merged pieces (all that tile_workspace_bytes provides for).
 int64_t tile_workspace_bytes(int G, int t_count, int pos0);
-hipError_t launch_tile_prepare(const RowArgs& a, int t_count, void* ws, hipStream_t stream);
-hipError_t launch_tile_attend(const RowArgs& a, int t_count, const void* ws, hipStream_t stream);
+int64_t tile_workspace_min_bytes(int G, int t_count, int pos0);
+hipError_t launch_tile_prepare(const RowArgs& a, int t_count, void* ws, int64_t ws_bytes,
+                               hipStream_t stream);
+hipError_t launch_tile_attend(const RowArgs& a, int t_count, void* ws, int64_t ws_bytes,
+                              hipStream_t stream);
 
 }  // namespace qsa

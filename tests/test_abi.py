@@ -59,7 +59,18 @@ def test_status_strings():
 def test_flash_workspace_size():
     # fused path: 64 KB per group and 64-cell chunk of the shared prefix
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=1984, pos0=0)) == 2 * 31 * 65536
-    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == 2 * 33 * 65536
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=1024, pos0=0)) == 2 * 16 * 65536
+    # a tiled grid of 64-query blocks that leaves CUs idle runs its blocks
+    # of at least 12 chunks as 2 or 3 pieces; the workspace then also holds,
+    # per split block, one partial slot per piece (64 x 256 floats of O, then
+    # (m, l) per query) and a 4-byte arrival counter (counters rounded up to
+    # 256 bytes).  T=512's blocks are at most 8 chunks: nothing is split.
+    # The budget-crossing chunk's one tiled token (pos0 2050) is one block
+    # per group, 33 chunks long: 3 pieces each.
+    slot = (64 * 256 + 2 * 64) * 4
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=512, pos0=0)) == 2 * 8 * 65536
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == \
+        2 * 33 * 65536 + 256 + 3 * 2 * slot
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=30000)) == 0
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=0, pos0=0)) == 0
 
@@ -215,8 +226,13 @@ def test_noalloc_checks_arguments_and_scratch_size_on_the_host():
     assert qsa.qsa_flash_workspace_bytes(big) > qsa.NOALLOC_SCRATCH_BYTES
     assert _raw(lib, "qsa_flash_noalloc", big, A, A, A, A, A, 0, A, 0, None) == \
         qsa.QSA_ERR_TOO_LARGE
-    # 2 groups up to an 8192-cell prefix fit exactly
+    # the chunk images of 2 groups up to an 8192-cell prefix fill the
+    # scratch exactly (qsa_flash_noalloc checks the images only); the full
+    # workspace adds room to split that token's one 128-chunk block per
+    # group into 3 pieces, which qsa_flash_noalloc then runs whole
     fit = qsa.QsaShape(T=1, pos0=8191, n_groups=2, budget=8192)
-    assert qsa.qsa_flash_workspace_bytes(fit) == qsa.NOALLOC_SCRATCH_BYTES
+    slot = (64 * 256 + 2 * 64) * 4
+    assert 2 * 128 * 65536 == qsa.NOALLOC_SCRATCH_BYTES
+    assert qsa.qsa_flash_workspace_bytes(fit) == qsa.NOALLOC_SCRATCH_BYTES + 256 + 3 * 2 * slot
     assert qsa.qsa_status_string(qsa.QSA_ERR_TOO_LARGE) != "unknown status"
     assert qsa.qsa_status_string(qsa.QSA_ERR_DEVICE) != "unknown status"
