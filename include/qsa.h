@@ -150,8 +150,9 @@ int qsa_topk(const qsa_shape *shape, const float *scores, int32_t *ids, void *st
  *              written.
  * Alignment: 16 bytes for q, kq, vq, out and part; 8 for ksc, vsc; 4 for ids;
  * 256 for workspace.
- * Numerics: fp16 MFMA products with fp32 accumulation (for rows above
- * budget the scores come from exact int8 products of the K codes with q
+ * Numerics: fp16 MFMA products with fp32 accumulation, k = code x scale
+ * rounded to fp16 (in fused mode, when more than 256 rows are above budget,
+ * their scores instead come from exact int8 products of the K codes with q
  * split into two int8 pieces, each element of q then within 2^-15 of the
  * head's largest |q|); relative L2 error against exact attention about
  * 4e-4 on the pages' value ranges.
@@ -186,7 +187,7 @@ int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq
 
 /*
  * Bytes of device workspace qsa_flash needs for this shape in fused mode
- * (0 when no token is under budget, and split mode needs none); a host-only
+ * (0 when it needs none, and split mode needs none); a host-only
  * helper.  The fused path dequantises the cells that tokens under budget
  * share -- cells [0, pos0 + t_id) of every group, t_id being the number of
  * such tokens -- once per call into this workspace: 64 KB per group and
@@ -197,7 +198,12 @@ int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq
  * partial results through the workspace; it then also holds, per split
  * block, one partial of 64 x 258 floats per piece and a 4-byte counter
  * (the counters rounded up to 256 bytes).  qsa_flash_prepare clears the
- * counters; every call leaves them at zero.
+ * counters; every call leaves them at zero.  When at most 256 (token,
+ * group) rows are above budget, they run as split mode's per-chunk records
+ * (part's layout, for those tokens) plus the merge, which fill the GPU
+ * where one wavefront per row would not; the records follow the part
+ * above, rounded up to 256 bytes, so such a call needs a workspace even
+ * with no token under budget.
  */
 int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
 

@@ -48,6 +48,37 @@ int identity_tokens(const qsa_shape* s) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
 
+// The fused path's workspace.  Its first part serves the tokens under
+// budget: the chunk images of their shared identity prefix, and room for
+// the split pieces of a tiled grid that leaves CUs idle.  When the rows
+// above budget are few, they run through the split kernel (one wavefront
+// per 64-cell chunk) and the merge instead of the row kernel (one
+// wavefront per row): a lone row takes the row kernel ~100 us, while the
+// split kernel's waves for up to kRowsSplitMax rows fill the GPU about
+// once; their records follow the first part.  The public calls ask for all
+// of it (qsa_flash_workspace_bytes); qsa_flash_noalloc asks only for the
+// chunk images and uses the rest as far as its scratch holds.
+constexpr int64_t kRowsSplitMax = 256;  // (token, group) rows above budget
+
+int64_t tile_part_bytes(const qsa_shape* s) {
+  const int64_t b = qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+  return (b + 255) / 256 * 256;
+}
+int64_t rows_record_bytes(const qsa_shape* s) {
+  const int64_t t_above = s->T - identity_tokens(s);
+  if (t_above <= 0 || t_above * s->n_groups > kRowsSplitMax) return 0;
+  const int64_t kc = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
+  return t_above * kc * s->n_groups * QSA_HEADS_PER_GROUP * QSA_PART_STRIDE * 4;
+}
+int64_t full_workspace(const qsa_shape* s) {
+  const int64_t rec = rows_record_bytes(s);
+  return rec > 0 ? tile_part_bytes(s) + rec
+                 : qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+}
+int64_t min_workspace(const qsa_shape* s) {
+  return qsa::tile_workspace_min_bytes(s->n_groups, identity_tokens(s), s->pos0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,7 +128,7 @@ int qsa_topk(const qsa_shape* s, const float* scores, int32_t* ids, void* stream
 
 int64_t qsa_flash_workspace_bytes(const qsa_shape* s) {
   if (check_shape(s) != QSA_OK) return 0;
-  return qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+  return full_workspace(s);
 }
 
 }  // extern "C"
@@ -131,16 +162,6 @@ int flash_args(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _F
   return QSA_OK;
 }
 
-// The fused path's workspace (needed for the identity prefix only): the
-// public calls ask for qsa_flash_workspace_bytes, which includes room for
-// the split pieces of a tiled grid that leaves CUs idle; qsa_flash_noalloc
-// asks only for the chunk images and splits as far as its scratch holds.
-int64_t full_workspace(const qsa_shape* s) {
-  return qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
-}
-int64_t min_workspace(const qsa_shape* s) {
-  return qsa::tile_workspace_min_bytes(s->n_groups, identity_tokens(s), s->pos0);
-}
 int check_workspace(const void* workspace, int64_t workspace_bytes, int64_t need) {
   if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need))
     return QSA_ERR_ARG;
@@ -181,6 +202,21 @@ int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _
   hipStream_t st = (hipStream_t)stream;
   rc = launch_status(qsa::launch_tile_attend(a, t_id, workspace, workspace_bytes, st));
   if (rc != QSA_OK) return rc;
+  const int64_t rec = rows_record_bytes(s);
+  if (rec > 0 && workspace_bytes >= tile_part_bytes(s) + rec) {
+    // tokens [t_id, T) as a shape of their own: split records, then merge
+    const int64_t H = (int64_t)s->n_groups * QSA_HEADS_PER_GROUP;
+    qsa::RowArgs b = a;
+    b.q = a.q + (int64_t)t_id * H * QSA_HEAD_DIM;
+    b.out = a.out + (int64_t)t_id * H * QSA_HEAD_DIM;
+    b.ids = a.ids + (int64_t)t_id * s->n_groups * s->budget;
+    b.T = s->T - t_id;
+    b.pos0 = s->pos0 + t_id;
+    b.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tile_part_bytes(s));
+    rc = launch_status(qsa::launch_flash_rows(b, true, 0, st));
+    if (rc != QSA_OK) return rc;
+    return launch_status(qsa::launch_merge(b.part, b.out, b.T, (int)H, b.pos0, s->budget, st));
+  }
   return launch_status(qsa::launch_flash_rows(a, false, t_id, st));
 }
 

@@ -69,9 +69,18 @@ def test_flash_workspace_size():
     # per group, 33 chunks long: 3 pieces each.
     slot = (64 * 256 + 2 * 64) * 4
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=512, pos0=0)) == 2 * 8 * 65536
+    tile = 2 * 33 * 65536 + 256 + 3 * 2 * slot
+    # up to 256 (token, group) rows above budget run as split records (the
+    # qsa_merge layout: 33 chunks x 24 heads x 258 floats per token) that
+    # follow the tiled part, rounded up to 256 bytes: the budget-crossing
+    # chunk's 95 tokens above budget
+    rec = 33 * 24 * 258 * 4
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == \
-        2 * 33 * 65536 + 256 + 3 * 2 * slot
-    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=30000)) == 0
+        (tile + 255) // 256 * 256 + 95 * rec
+    # no token under budget: the records alone; past 256 rows the row
+    # kernel needs no workspace
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=30000)) == 96 * rec
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=129, pos0=30000)) == 0
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=0, pos0=0)) == 0
 
 

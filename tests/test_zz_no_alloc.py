@@ -1,7 +1,11 @@
 """qsa_flash_noalloc (library-held scratch, no workspace argument) against
-qsa_flash with a caller workspace: same bytes, and the oracle's bar, on two
-calls in a row of which the second is smaller (the scratch keeps the first
-call's images; the second must not read them)."""
+qsa_flash with a caller workspace, on two calls in a row of which the
+second is smaller (the scratch keeps the first call's images; the second
+must not read them): the same bytes when qsa_flash's whole workspace fits
+the scratch (both calls then take the same kernels), otherwise the same
+output within the oracle's bar (the scratch holds the chunk images but not
+the records of the split rows, which then run on the row kernel); and the
+oracle's bar in every case."""
 import numpy as np
 import pytest
 import torch
@@ -41,7 +45,12 @@ def test_noalloc_matches_workspace_call_twice(cases):
             ids = oracle.select(T, pos0, inp.budget, inp.scores, 2, inp.n_cells)
         dev = upload(inp)
         got = _noalloc(inp, ids, dev)
-        np.testing.assert_array_equal(got, _with_workspace(inp, ids, dev))
+        full = _with_workspace(inp, ids, dev)
+        if qsa.qsa_flash_workspace_bytes(shape_of(inp)) <= qsa.NOALLOC_SCRATCH_BYTES:
+            np.testing.assert_array_equal(got, full)
+        else:
+            assert oracle.rel_l2(got, full) <= 1e-3
+            assert worst_row_rel_l2(got, full) <= 4e-3
         ref = oracle.attend(inp, ids)
         assert oracle.rel_l2(got, ref) <= 1e-3
         assert worst_row_rel_l2(got, ref) <= 4e-3
