@@ -202,8 +202,10 @@ int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq
  * group) rows are above budget, they run as split mode's per-chunk records
  * (part's layout, for those tokens) plus the merge, which fill the GPU
  * where one wavefront per row would not; the records follow the part
- * above, rounded up to 256 bytes, so such a call needs a workspace even
- * with no token under budget.
+ * above, rounded up to 256 bytes.  When the whole call has at most 256
+ * rows and some above budget, every token runs that way and the workspace
+ * holds the records alone (qsa_flash_prepare then enqueues nothing).  Such
+ * calls need a workspace even with no token under budget.
  */
 int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
 

@@ -48,32 +48,52 @@ int identity_tokens(const qsa_shape* s) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
 
-// The fused path's workspace.  Its first part serves the tokens under
-// budget: the chunk images of their shared identity prefix, and room for
-// the split pieces of a tiled grid that leaves CUs idle.  When the rows
-// above budget are few, they run through the split kernel (one wavefront
-// per 64-cell chunk) and the merge instead of the row kernel (one
-// wavefront per row): a lone row takes the row kernel ~100 us, while the
-// split kernel's waves for up to kRowsSplitMax rows fill the GPU about
-// once; their records follow the first part.  The public calls ask for all
-// of it (qsa_flash_workspace_bytes); qsa_flash_noalloc asks only for the
-// chunk images and uses the rest as far as its scratch holds.
-constexpr int64_t kRowsSplitMax = 256;  // (token, group) rows above budget
+// How a fused call runs, and its workspace.  Tokens under budget share a
+// prefix of cells: the tiled path dequantises it once (the chunk images,
+// plus room for the split pieces of a tiled grid that leaves CUs idle) and
+// attends from it.  Rows above budget run on the row kernel, one wavefront
+// per row; when they are few (at most kRowsSplitMax) they run instead as
+// split records (one wavefront per 64-cell chunk) plus the merge, whose
+// waves fill the GPU where a lone row would take the row kernel ~100 us.
+// Their records follow the tiled part.  When the whole call has at most
+// kRowsSplitMax rows and some above budget, every token runs that way (the
+// few tokens under budget gain nothing from the tiled path's two extra
+// launches), with the records alone in the workspace.  The public calls
+// ask for the whole workspace of the route (qsa_flash_workspace_bytes);
+// qsa_flash_noalloc asks only for the chunk images, and takes a split
+// route only when its scratch holds that route's records.
+constexpr int64_t kRowsSplitMax = 256;  // (token, group) rows
 
+enum class Route { kRows, kSplitRows, kAllSplit };
+
+Route route_of(const qsa_shape* s) {
+  const int64_t t_above = s->T - identity_tokens(s);
+  if (t_above <= 0) return Route::kRows;  // no row above budget
+  if ((int64_t)s->T * s->n_groups <= kRowsSplitMax) return Route::kAllSplit;
+  if (t_above * s->n_groups <= kRowsSplitMax) return Route::kSplitRows;
+  return Route::kRows;
+}
+int64_t record_bytes(const qsa_shape* s, int64_t tokens) {
+  const int64_t kc = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
+  return tokens * kc * s->n_groups * QSA_HEADS_PER_GROUP * QSA_PART_STRIDE * 4;
+}
 int64_t tile_part_bytes(const qsa_shape* s) {
   const int64_t b = qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
   return (b + 255) / 256 * 256;
 }
-int64_t rows_record_bytes(const qsa_shape* s) {
-  const int64_t t_above = s->T - identity_tokens(s);
-  if (t_above <= 0 || t_above * s->n_groups > kRowsSplitMax) return 0;
-  const int64_t kc = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
-  return t_above * kc * s->n_groups * QSA_HEADS_PER_GROUP * QSA_PART_STRIDE * 4;
-}
 int64_t full_workspace(const qsa_shape* s) {
-  const int64_t rec = rows_record_bytes(s);
-  return rec > 0 ? tile_part_bytes(s) + rec
-                 : qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+  switch (route_of(s)) {
+    case Route::kAllSplit: return record_bytes(s, s->T);
+    case Route::kSplitRows: return tile_part_bytes(s) + record_bytes(s, s->T - identity_tokens(s));
+    default: return qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
+  }
+}
+// The route a call with workspace_bytes of scratch takes: a split route
+// only when the scratch holds its workspace.
+Route route_with(const qsa_shape* s, int64_t workspace_bytes) {
+  const Route r = route_of(s);
+  if (r != Route::kRows && workspace_bytes < full_workspace(s)) return Route::kRows;
+  return r;
 }
 int64_t min_workspace(const qsa_shape* s) {
   return qsa::tile_workspace_min_bytes(s->n_groups, identity_tokens(s), s->pos0);
@@ -183,6 +203,7 @@ int prepare_impl(const qsa_shape* s, const int8_t* kq, const _Float16* ksc, cons
   int rc = flash_args(s, nullptr, kq, ksc, vq, vsc, nullptr, nullptr, nullptr, &a);
   if (rc == QSA_OK) rc = check_workspace(workspace, workspace_bytes, need);
   if (rc != QSA_OK) return rc;
+  if (route_with(s, workspace_bytes) == Route::kAllSplit) return QSA_OK;  // nothing to prepare
   return launch_status(qsa::launch_tile_prepare(a, identity_tokens(s), workspace,
                                                 workspace_bytes, (hipStream_t)stream));
 }
@@ -199,24 +220,27 @@ int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _
   // cells, dequantised once into the workspace and shared by the tiled
   // kernel; tokens above budget gather their own ids row by row
   const int t_id = identity_tokens(s);
+  const int64_t H = (int64_t)s->n_groups * QSA_HEADS_PER_GROUP;
   hipStream_t st = (hipStream_t)stream;
+  // tokens [t0, T) as a shape of their own: split records in the workspace
+  // from byte `off`, then the merge into out
+  auto split_tokens = [&](int t0, int64_t off) {
+    qsa::RowArgs b = a;
+    b.q = a.q + (int64_t)t0 * H * QSA_HEAD_DIM;
+    b.out = a.out + (int64_t)t0 * H * QSA_HEAD_DIM;
+    if (a.ids) b.ids = a.ids + (int64_t)t0 * s->n_groups * s->budget;
+    b.T = s->T - t0;
+    b.pos0 = s->pos0 + t0;
+    b.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off);
+    int r = launch_status(qsa::launch_flash_rows(b, true, 0, st));
+    if (r != QSA_OK) return r;
+    return launch_status(qsa::launch_merge(b.part, b.out, b.T, (int)H, b.pos0, s->budget, st));
+  };
+  const Route route = route_with(s, workspace_bytes);
+  if (route == Route::kAllSplit) return split_tokens(0, 0);
   rc = launch_status(qsa::launch_tile_attend(a, t_id, workspace, workspace_bytes, st));
   if (rc != QSA_OK) return rc;
-  const int64_t rec = rows_record_bytes(s);
-  if (rec > 0 && workspace_bytes >= tile_part_bytes(s) + rec) {
-    // tokens [t_id, T) as a shape of their own: split records, then merge
-    const int64_t H = (int64_t)s->n_groups * QSA_HEADS_PER_GROUP;
-    qsa::RowArgs b = a;
-    b.q = a.q + (int64_t)t_id * H * QSA_HEAD_DIM;
-    b.out = a.out + (int64_t)t_id * H * QSA_HEAD_DIM;
-    b.ids = a.ids + (int64_t)t_id * s->n_groups * s->budget;
-    b.T = s->T - t_id;
-    b.pos0 = s->pos0 + t_id;
-    b.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tile_part_bytes(s));
-    rc = launch_status(qsa::launch_flash_rows(b, true, 0, st));
-    if (rc != QSA_OK) return rc;
-    return launch_status(qsa::launch_merge(b.part, b.out, b.T, (int)H, b.pos0, s->budget, st));
-  }
+  if (route == Route::kSplitRows) return split_tokens(t_id, tile_part_bytes(s));
   return launch_status(qsa::launch_flash_rows(a, false, t_id, st));
 }
 

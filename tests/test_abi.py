@@ -65,20 +65,21 @@ def test_flash_workspace_size():
     # per split block, one partial slot per piece (64 x 256 floats of O, then
     # (m, l) per query) and a 4-byte arrival counter (counters rounded up to
     # 256 bytes).  T=512's blocks are at most 8 chunks: nothing is split.
-    # The budget-crossing chunk's one tiled token (pos0 2050) is one block
-    # per group, 33 chunks long: 3 pieces each.
     slot = (64 * 256 + 2 * 64) * 4
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=512, pos0=0)) == 2 * 8 * 65536
-    tile = 2 * 33 * 65536 + 256 + 3 * 2 * slot
     # up to 256 (token, group) rows above budget run as split records (the
-    # qsa_merge layout: 33 chunks x 24 heads x 258 floats per token) that
-    # follow the tiled part, rounded up to 256 bytes: the budget-crossing
-    # chunk's 95 tokens above budget
+    # qsa_merge layout: 33 chunks x 24 heads x 258 floats per token) after
+    # the tiled part (rounded up to 256 bytes): T=200 at pos0 1900 tiles its
+    # 151 tokens under budget (29 blocks of 64 queries per group, 33 chunks
+    # each, in 3 pieces) and splits its 49 tokens above
     rec = 33 * 24 * 258 * 4
-    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == \
-        (tile + 255) // 256 * 256 + 95 * rec
-    # no token under budget: the records alone; past 256 rows the row
-    # kernel needs no workspace
+    tile = 2 * 33 * 65536 + 256 + 3 * (2 * 29) * slot
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=200, pos0=1900)) == \
+        (tile + 255) // 256 * 256 + 49 * rec
+    # a call of at most 256 rows with some above budget splits every token
+    # (the budget-crossing chunk), and with none under budget as well; past
+    # 256 rows above budget the row kernel needs no workspace
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == 96 * rec
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=30000)) == 96 * rec
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=129, pos0=30000)) == 0
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=0, pos0=0)) == 0
