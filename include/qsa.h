@@ -229,7 +229,10 @@ int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
  *   QSA_ERR_DEVICE when the device or the array's address cannot be
  *   queried.  The scratch beyond the images holds the split pieces that
  *   qsa_flash_workspace_bytes makes room for, as far as it reaches; blocks
- *   it cannot hold run whole, which changes the output only by rounding.
+ *   it cannot hold run whole.  Rows above budget run as split records plus
+ *   the merge, as in qsa_flash, when qsa_flash_workspace_bytes fits the
+ *   scratch whole, and on the row kernel otherwise.  Either difference
+ *   changes the output only by rounding.
  */
 int qsa_flash_noalloc(const qsa_shape *shape, const _Float16 *q, const int8_t *kq,
                       const _Float16 *ksc, const int8_t *vq, const _Float16 *vsc,

@@ -356,13 +356,18 @@ int qsa_flash_noalloc(const qsa_shape* s, const _Float16* q, const int8_t* kq,
   }
   const int64_t need = part ? 0 : min_workspace(s);
   if (need > QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_TOO_LARGE;
+  // the scratch holds the chunk images, and the split records of a route
+  // that uses them when the route's whole workspace fits (with no token
+  // under budget, only then is it needed)
+  const int64_t full = part ? 0 : full_workspace(s);
+  const bool use = need > 0 || (full > 0 && full <= QSA_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
-  if (need > 0) {
+  if (use) {
     ws = scratch_ptr();
     if (!ws) return QSA_ERR_DEVICE;
   }
   return flash_impl(s, q, kq, ksc, vq, vsc, ids, out, part, ws,
-                    need > 0 ? (int64_t)QSA_NOALLOC_SCRATCH_BYTES : 0, stream, need);
+                    use ? (int64_t)QSA_NOALLOC_SCRATCH_BYTES : 0, stream, need);
 }
 
 }  // extern "C"

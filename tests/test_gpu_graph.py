@@ -148,7 +148,7 @@ def test_graph_prepare_then_attend():
     _check_replays(run, [out])
 
 
-@pytest.mark.parametrize("T,pos0", [(96, 0), (1984, 0), (200, 1900)])
+@pytest.mark.parametrize("T,pos0", [(96, 0), (1984, 0), (200, 1900), (96, 2050)])
 def test_graph_noalloc(T, pos0):
     """The no-alloc call, whose scratch the eager work between replays
     overwrites with another shape's images."""

@@ -3,9 +3,10 @@ qsa_flash with a caller workspace, on two calls in a row of which the
 second is smaller (the scratch keeps the first call's images; the second
 must not read them): the same bytes when qsa_flash's whole workspace fits
 the scratch (both calls then take the same kernels), otherwise the same
-output within the oracle's bar (the scratch holds the chunk images but not
-the records of the split rows, which then run on the row kernel); and the
-oracle's bar in every case."""
+output within the oracle's bar (the scratch holds the chunk images, but a
+split route whose whole workspace it cannot hold leaves those rows to the
+row kernel); and the oracle's bar in every case.  The last pair has no
+token under budget: only the split records use the scratch."""
 import numpy as np
 import pytest
 import torch
@@ -36,7 +37,8 @@ def _with_workspace(inp, ids, dev):
     return out.numpy("qsa_flash out").astype(np.float64)
 
 
-@pytest.mark.parametrize("cases", [((1984, 0, 3), (512, 0, 4)), ((200, 1900, 1), (33, 0, 2))])
+@pytest.mark.parametrize("cases", [((1984, 0, 3), (512, 0, 4)), ((200, 1900, 1), (33, 0, 2)),
+                                   ((96, 2050, 5), (32, 2050, 6))])
 def test_noalloc_matches_workspace_call_twice(cases):
     for T, pos0, layer in cases:       # the second call is the smaller one
         inp = qsa_synth.layer_inputs(T, pos0, layer=layer)
