@@ -151,11 +151,12 @@ int qsa_topk(const qsa_shape *shape, const float *scores, int32_t *ids, void *st
  * Alignment: 16 bytes for q, kq, vq, out and part; 8 for ksc, vsc; 4 for ids;
  * 256 for workspace.
  * Numerics: fp16 MFMA products with fp32 accumulation, k = code x scale
- * rounded to fp16 (in fused mode, when more than 256 rows are above budget,
- * their scores instead come from exact int8 products of the K codes with q
- * split into two int8 pieces, each element of q then within 2^-15 of the
- * head's largest |q|); relative L2 error against exact attention about
- * 4e-4 on the pages' value ranges.
+ * rounded to fp16 (in fused mode, rows above budget, and every row of a call
+ * that runs as row pieces, instead take their scores from exact int8
+ * products of the K codes with q split into two int8 pieces, each element
+ * of q then within 2^-15 of the head's largest |q|, unless so few rows run
+ * that each piece is one chunk); relative L2 error against exact attention
+ * about 4e-4 on the pages' value ranges.
  */
 int qsa_flash(const qsa_shape *shape, const _Float16 *q, const int8_t *kq, const _Float16 *ksc,
               const int8_t *vq, const _Float16 *vsc, const int32_t *ids, _Float16 *out,
@@ -199,13 +200,16 @@ int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq
  * block, one partial of 64 x 258 floats per piece and a 4-byte counter
  * (the counters rounded up to 256 bytes).  qsa_flash_prepare clears the
  * counters; every call leaves them at zero.  When at most 256 (token,
- * group) rows are above budget, they run as split mode's per-chunk records
- * (part's layout, for those tokens) plus the merge, which fill the GPU
- * where one wavefront per row would not; the records follow the part
- * above, rounded up to 256 bytes.  When the whole call has at most 256
- * rows and some above budget, every token runs that way and the workspace
- * holds the records alone (qsa_flash_prepare then enqueues nothing).  Such
- * calls need a workspace even with no token under budget.
+ * group) rows are above budget, they run as row pieces plus the merge,
+ * which fill the GPU where one wavefront per row would not.  Each row is
+ * cut into pieces of cpr consecutive 64-cell chunks of its selection,
+ * cpr = ceil(rows x ceil(budget/64) / 1024), and each piece writes one
+ * (o, m, l) record of 258 floats per head (part's layout with a record per
+ * piece instead of per chunk).  The records follow the part above, rounded
+ * up to 256 bytes.  When the whole call has at most 256 rows and some above
+ * budget, every token runs that way and the workspace holds the records
+ * alone (qsa_flash_prepare then enqueues nothing).  Such calls need a
+ * workspace even with no token under budget.
  */
 int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
 
@@ -229,10 +233,10 @@ int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
  *   QSA_ERR_DEVICE when the device or the array's address cannot be
  *   queried.  The scratch beyond the images holds the split pieces that
  *   qsa_flash_workspace_bytes makes room for, as far as it reaches; blocks
- *   it cannot hold run whole.  Rows above budget run as split records plus
- *   the merge, as in qsa_flash, when qsa_flash_workspace_bytes fits the
- *   scratch whole, and on the row kernel otherwise.  Either difference
- *   changes the output only by rounding.
+ *   it cannot hold run whole.  Rows above budget run as row pieces plus the
+ *   merge, as in qsa_flash, when qsa_flash_workspace_bytes fits the scratch
+ *   whole, and on the row kernel otherwise.  Either difference changes the
+ *   output only by rounding.
  */
 int qsa_flash_noalloc(const qsa_shape *shape, const _Float16 *q, const int8_t *kq,
                       const _Float16 *ksc, const int8_t *vq, const _Float16 *vsc,

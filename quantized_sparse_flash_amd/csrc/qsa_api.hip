@@ -53,12 +53,13 @@ int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUN
 // plus room for the split pieces of a tiled grid that leaves CUs idle) and
 // attends from it.  Rows above budget run on the row kernel, one wavefront
 // per row; when they are few (at most kRowsSplitMax) they run instead as
-// split records (one wavefront per 64-cell chunk) plus the merge, whose
-// waves fill the GPU where a lone row would take the row kernel ~100 us.
-// Their records follow the tiled part.  When the whole call has at most
-// kRowsSplitMax rows and some above budget, every token runs that way (the
-// few tokens under budget gain nothing from the tiled path's two extra
-// launches), with the records alone in the workspace.  The public calls
+// row pieces (one wavefront per piece of a few 64-cell chunks, about
+// kPieceWaves wavefronts in all) plus the merge, which fill the GPU where
+// a lone row would take the row kernel ~100 us.  Their records follow the
+// tiled part.  When the whole call has at most kRowsSplitMax rows and some
+// above budget, every token runs that way (the few tokens under budget
+// gain nothing from the tiled path's two extra launches), with the records
+// alone in the workspace.  The public calls
 // ask for the whole workspace of the route (qsa_flash_workspace_bytes);
 // qsa_flash_noalloc asks only for the chunk images, and takes a split
 // route only when its scratch holds that route's records.
@@ -73,9 +74,20 @@ Route route_of(const qsa_shape* s) {
   if (t_above * s->n_groups <= kRowsSplitMax) return Route::kSplitRows;
   return Route::kRows;
 }
+// Chunks per record of the row pieces of `rows` (token, group) rows: about
+// kPieceWaves wavefronts in all, one per SIMD, a piece at least one chunk
+// (measured against 512 to 4096: fewer, longer pieces amortise the staged
+// pipeline's start; fewer wavefronts than SIMDs leave the GPU idle).
+constexpr int64_t kPieceWaves = 1024;
+int pieces_cpr(int64_t rows, int kc) {
+  const int64_t c = (rows * kc + kPieceWaves - 1) / kPieceWaves;
+  return (int)(c < 1 ? 1 : (c > kc ? kc : c));
+}
 int64_t record_bytes(const qsa_shape* s, int64_t tokens) {
-  const int64_t kc = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
-  return tokens * kc * s->n_groups * QSA_HEADS_PER_GROUP * QSA_PART_STRIDE * 4;
+  const int kc = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
+  const int cpr = pieces_cpr(tokens * s->n_groups, kc);
+  const int64_t kcr = (kc + cpr - 1) / cpr;
+  return tokens * kcr * s->n_groups * QSA_HEADS_PER_GROUP * QSA_PART_STRIDE * 4;
 }
 int64_t tile_part_bytes(const qsa_shape* s) {
   const int64_t b = qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
@@ -177,6 +189,7 @@ int flash_args(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _F
   a->G = s->n_groups;
   a->budget = s->budget;
   a->KC = (s->budget + QSA_CHUNK - 1) / QSA_CHUNK;
+  a->cpr = 1;
   a->n_items = 0;
   a->n_cells = s->n_cells;
   return QSA_OK;
@@ -222,8 +235,8 @@ int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _
   const int t_id = identity_tokens(s);
   const int64_t H = (int64_t)s->n_groups * QSA_HEADS_PER_GROUP;
   hipStream_t st = (hipStream_t)stream;
-  // tokens [t0, T) as a shape of their own: split records in the workspace
-  // from byte `off`, then the merge into out
+  // tokens [t0, T) as a shape of their own: row-piece records in the
+  // workspace from byte `off`, then the merge into out
   auto split_tokens = [&](int t0, int64_t off) {
     qsa::RowArgs b = a;
     b.q = a.q + (int64_t)t0 * H * QSA_HEAD_DIM;
@@ -232,9 +245,14 @@ int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _
     b.T = s->T - t0;
     b.pos0 = s->pos0 + t0;
     b.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off);
-    int r = launch_status(qsa::launch_flash_rows(b, true, 0, st));
+    b.cpr = pieces_cpr((int64_t)b.T * s->n_groups, b.KC);
+    // one chunk per record: the split kernel, which loads its chunk at once
+    // (the same record layout); longer pieces: the staged row kernel
+    int r = launch_status(b.cpr == 1 ? qsa::launch_flash_rows(b, true, 0, st)
+                                     : qsa::launch_flash_row_pieces(b, st));
     if (r != QSA_OK) return r;
-    return launch_status(qsa::launch_merge(b.part, b.out, b.T, (int)H, b.pos0, s->budget, st));
+    return launch_status(
+        qsa::launch_merge(b.part, b.out, b.T, (int)H, b.pos0, s->budget, b.cpr, st));
   };
   const Route route = route_with(s, workspace_bytes);
   if (route == Route::kAllSplit) return split_tokens(0, 0);
@@ -300,7 +318,7 @@ int qsa_merge(const qsa_shape* s, const float* part, _Float16* out, void* stream
   if (rc != QSA_OK) return rc;
   if (!part || !out || !aligned(part, 16) || !aligned(out, 16)) return QSA_ERR_ARG;
   return launch_status(qsa::launch_merge(part, out, s->T, s->n_groups * QSA_HEADS_PER_GROUP,
-                                         s->pos0, s->budget, (hipStream_t)stream));
+                                         s->pos0, s->budget, 1, (hipStream_t)stream));
 }
 
 int qsa_quantize(int64_t n_rows, int32_t dim, const _Float16* x, int8_t* codes,

@@ -295,15 +295,27 @@ __device__ __forceinline__ void wait_lds_reads() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // the same wait, seen by the compiler
 }
 
-template <bool WIDE>
+// PIECES: each wavefront attends one piece of a row, a.cpr consecutive
+// 64-cell chunks of its selection (piece p: chunks a.cpr p ..), and writes
+// the piece's (o, m, l) record for the merge instead of the row's output;
+// a row under budget then takes its cells by position.
+template <bool WIDE, bool PIECES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_rows_staged_kernel(RowArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t img_all[4][kImgBytes];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int G = a.G, H = G * kHpg;
-  int t, g;
-  if (kXcds % G == 0) {
+  const int kcr = (a.KC + a.cpr - 1) / a.cpr;  // records per row (PIECES)
+  int t, g, piece = 0;
+  if constexpr (PIECES) {
+    // (token, group, piece) per wavefront, a row's pieces consecutive
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+    if (item >= a.n_items) return;
+    piece = item % kcr;
+    g = (item / kcr) % G;
+    t = item / (kcr * G);
+  } else if (kXcds % G == 0) {
     // workgroups are dealt to the XCDs round robin: XCD x serves group
     // x % G only, so each XCD's L2 caches one group's cells
     const int per = kXcds / G;
@@ -321,10 +333,23 @@ void flash_rows_staged_kernel(RowArgs a) {
   uint8_t* img = img_all[wave];
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(rows_lds_addr(img));  // wave-uniform
 
-  // only rows above budget come here (the tile kernel attends the rest):
-  // every row selects exactly `budget` cells through its ids
-  const int nsel = a.budget;
+  // Without PIECES only rows above budget come here (the tile kernel attends
+  // the rest): every row selects exactly `budget` cells through its ids.  A
+  // piece's row may be under budget (identity: cell = position); its ids
+  // are then never read, and the ids copies, which keep the copy counts of
+  // the waits below, read the launch's last row instead (above budget).
+  const int64_t nkv = (int64_t)a.pos0 + t + 1;
+  const bool identity = PIECES && nkv <= a.budget;
+  const int nsel = identity ? (int)nkv : a.budget;
   const int nst = (nsel + kStage - 1) / kStage;
+  int k_begin = 0, s_end = nst;  // this wavefront's chunks and stages
+  if constexpr (PIECES) {
+    const int nch = (nsel + kChunk - 1) / kChunk;
+    k_begin = piece * a.cpr;
+    if (k_begin >= nch) return;
+    s_end = min(2 * min(k_begin + a.cpr, nch), nst);
+  }
+  const int s_begin = 2 * k_begin;
 
   const int n = lane & 15, j = lane >> 4;
   const bool qvalid = n < kHpg;
@@ -375,7 +400,7 @@ void flash_rows_staged_kernel(RowArgs a) {
   const int8_t* vq_g = a.vq + (int64_t)g * a.n_cells * kHeadDim;
   const _Float16* ksc_g = a.ksc + (int64_t)g * a.n_cells * kNBlk;
   const _Float16* vsc_g = a.vsc + (int64_t)g * a.n_cells * kNBlk;
-  const int32_t* ids_row = a.ids + ((int64_t)t * G + g) * a.budget;
+  const int32_t* ids_row = a.ids + ((int64_t)(identity ? a.T - 1 : t) * G + g) * a.budget;
   auto clamp_cell = [&](int c) -> int {
     c = c < 0 ? 0 : c;
     return (int64_t)c >= a.n_cells ? (int)(a.n_cells - 1) : c;
@@ -435,25 +460,27 @@ void flash_rows_staged_kernel(RowArgs a) {
   // stage s + 1 in its V phase, each from offsets computed one phase pair
   // earlier (the shuffles' latency hides behind a PV).  The ids of chunk
   // k + 2 are copied in stage 2 k's V phase, just before V of stage 2 k + 1,
-  // and read out in stage 2 k + 2's.  Chunks 0 and 1 come from plain loads.
+  // and read out in stage 2 k + 2's.  The wavefront's first two chunks come
+  // from plain loads.
+  auto position = [&](int k) { return min(k * kChunk + lane, nsel - 1); };
   int ids_next;
   int cells[kCopiesPerHalf];  // cells of the next stage's copies
   Off offs[kCopiesPerHalf];
   {
-    const int ids0 = clamp_cell(ids_row[min(lane, nsel - 1)]);
-    ids_next = clamp_cell(ids_row[min(kChunk + lane, nsel - 1)]);
+    const int ids0 = identity ? position(k_begin) : clamp_cell(ids_row[position(k_begin)]);
+    ids_next = identity ? position(k_begin + 1) : clamp_cell(ids_row[position(k_begin + 1)]);
     // both loads complete before the first copy (the copies' waits count
     // copies only)
     asm volatile("" : : "v"(ids0), "v"(ids_next));
-    cells_of(0, ids0, cells);
+    cells_of(s_begin, ids0, cells);
     offsets_of(cells, offs);
     issue_half(offs, kq_g, ksc_g, kImgK, kImgKs);
     issue_half(offs, vq_g, vsc_g, kImgV, kImgVs);
-    cells_of(1, ids0, cells);
+    cells_of(s_begin + 1, ids0, cells);
   }
 
-  for (int s = 0; s < nst; ++s) {
-    const bool more = s + 1 < nst;
+  for (int s = s_begin; s < s_end; ++s) {
+    const bool more = s + 1 < s_end;
     const bool even = (s & 1) == 0;
     const int k = s >> 1;
     // ---- K phase: K of stage s into registers, K of stage s + 1 started.
@@ -547,11 +574,11 @@ void flash_rows_staged_kernel(RowArgs a) {
                                                 16 * (n ^ (row & 15)));
       sp[i >> 1][i & 1] = *reinterpret_cast<const _Float16*>(img + kImgVs + 8 * c + 2 * (n >> 2));
     }
-    const bool new_chunk = even && k >= 1;  // the ids of chunk k + 1 are due
+    const bool new_chunk = even && k > k_begin;  // the ids of chunk k + 1 are due
     int ids_raw = 0;
     if (new_chunk) ids_raw = *reinterpret_cast<const int*>(img + kImgIds + 4 * lane);
     wait_lds_reads();
-    if (new_chunk) ids_next = clamp_cell(ids_raw);
+    if (new_chunk) ids_next = identity ? position(k + 1) : clamp_cell(ids_raw);
     if (more) {
       if (even) issue_ids(k + 2);
       issue_half(offs, vq_g, vsc_g, kImgV, kImgVs);
@@ -576,6 +603,17 @@ void flash_rows_staged_kernel(RowArgs a) {
 
   const float l_tot = wave_sum_xor16_32(l_run);
   if (!qvalid) return;
+  if constexpr (PIECES) {
+    // the piece's record: O unnormalised, m in natural-log units, l
+    float* rec = a.part + (((int64_t)t * kcr + piece) * H + hq) * kRec;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int mt = 0; mt < 16; mt += 2)
+        *reinterpret_cast<float2*>(rec + 64 * j + 16 * r + mt) = float2{oacc[mt][r], oacc[mt + 1][r]};
+    if (j == 0) *reinterpret_cast<float2*>(rec + kHeadDim) = float2{m_run * kLn2, l_tot};
+    return;
+  }
   const float inv = 1.f / l_tot;
   _Float16* orow = a.out + ((int64_t)t * H + hq) * kHeadDim + 64 * j;
 #pragma unroll
@@ -609,9 +647,25 @@ hipError_t launch_flash_rows(const RowArgs& args_in, bool split, int t_begin,
   if (split)
     flash_split_kernel<<<grid, block, 0, stream>>>(a);
   else if (a.n_cells <= (int64_t(1) << 24))
-    flash_rows_staged_kernel<false><<<grid, block, 0, stream>>>(a);
+    flash_rows_staged_kernel<false, false><<<grid, block, 0, stream>>>(a);
   else
-    flash_rows_staged_kernel<true><<<grid, block, 0, stream>>>(a);
+    flash_rows_staged_kernel<true, false><<<grid, block, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flash_row_pieces(const RowArgs& args_in, hipStream_t stream) {
+  RowArgs a = args_in;
+  if (a.T <= 0) return hipSuccess;
+  // the ids copies of rows under budget read the last row: it must be above
+  if (a.cpr < 1 || !a.part || !a.ids || (int64_t)a.pos0 + a.T <= a.budget)
+    return hipErrorInvalidValue;
+  const int kcr = (a.KC + a.cpr - 1) / a.cpr;
+  a.n_items = a.T * a.G * kcr;
+  dim3 grid((a.n_items + 3) / 4), block(256);
+  if (a.n_cells <= (int64_t(1) << 24))
+    flash_rows_staged_kernel<false, true><<<grid, block, 0, stream>>>(a);
+  else
+    flash_rows_staged_kernel<true, true><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 

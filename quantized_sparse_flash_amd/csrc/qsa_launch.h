@@ -17,6 +17,7 @@ struct RowArgs {
   _Float16* out;
   float* part;
   int T, pos0, G, budget, KC, n_items;
+  int cpr;  // chunks per record of the row pieces (launch_flash_row_pieces)
   int64_t n_cells;
 };
 
@@ -25,8 +26,9 @@ hipError_t launch_score(const float* qidx, const float* pooled, float* scores, i
                         int G, int budget, int64_t n_cells, int dim, hipStream_t stream);
 hipError_t launch_topk(const float* scores, int32_t* ids, int T, int pos0, int G, int budget,
                        int64_t n_cells, hipStream_t stream);
+// Merge of records that cover cpr chunks each (1: the split-mode records).
 hipError_t launch_merge(const float* part, _Float16* out, int T, int H, int pos0, int budget,
-                        hipStream_t stream);
+                        int cpr, hipStream_t stream);
 // K/V quantiser: `rows` fp16 rows of 256 dims -> int8 codes and 4 fp16
 // scales per row.
 hipError_t launch_quantize(const _Float16* x, int8_t* codes, _Float16* scales, int64_t rows,
@@ -35,6 +37,10 @@ hipError_t launch_quantize(const _Float16* x, int8_t* codes, _Float16* scales, i
 // all of which must be above budget (fused), or per (token, group, chunk)
 // for all tokens (split mode).
 hipError_t launch_flash_rows(const RowArgs& a, bool split, int t_begin, hipStream_t stream);
+// Row pieces: one wavefront per (token, group, piece of a.cpr chunks) of
+// every token, each writing that piece's (o, m, l) record into a.part
+// ([T][ceil(KC / cpr)][G*12][258]); the last token must be above budget.
+hipError_t launch_flash_row_pieces(const RowArgs& a, hipStream_t stream);
 // Tile path: fused attention of tokens [0, t_count), all under budget.
 // launch_tile_prepare dequantises cells [0, pos0 + t_count) of every group
 // into `ws` (ws_bytes bytes, at least tile_workspace_min_bytes) and clears

@@ -6,6 +6,10 @@
 // records (o_k, m_k, l_k):
 //   M = max_k m_k,  L = sum_k l_k e^(m_k - M),  out = sum_k e^(m_k - M) o_k / L.
 //
+// Records may also cover cpr consecutive chunks each (the row pieces of a
+// fused call): nk = ceil(ceil(n_sel(t)/64) / cpr) records per token, KC
+// record slots per token in the array.
+//
 // Two wavefronts per (token, head), one per 128-dim half.  A pass over up to
 // 32 records issues all of its loads at once -- lane i reads record i's
 // (m, l), every lane reads its two dims of every record -- so a merge costs
@@ -23,7 +27,7 @@ constexpr int kGroup = 32;
 
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
                                                     _Float16* __restrict__ out, int T, int H,
-                                                    int pos0, int budget, int KC) {
+                                                    int pos0, int budget, int KC, int cpr) {
   const int lane = threadIdx.x & 63;
   // wave-uniform: two waves per (token, head), one per 128-dim half
   const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
@@ -32,7 +36,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int t = pair / H, h = pair % H;
   const int64_t nkv = (int64_t)pos0 + t + 1;
   const int nsel = nkv < budget ? (int)nkv : budget;
-  const int nk = (nsel + kChunk - 1) / kChunk;
+  const int nk = ((nsel + kChunk - 1) / kChunk + cpr - 1) / cpr;
   const float* base = part + ((int64_t)t * KC * H + h) * kRec;
   const int64_t kstride = (int64_t)H * kRec;
   const int d0 = 128 * half + 2 * lane;  // this lane's two output dims
@@ -77,11 +81,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 }
 
 hipError_t launch_merge(const float* part, _Float16* out, int T, int H, int pos0, int budget,
-                        hipStream_t stream) {
-  const int KC = (budget + kChunk - 1) / kChunk;
+                        int cpr, hipStream_t stream) {
+  if (cpr < 1) return hipErrorInvalidValue;
+  const int KC = ((budget + kChunk - 1) / kChunk + cpr - 1) / cpr;
   const int waves = 2 * T * H;
   dim3 grid((waves + 3) / 4), block(256);
-  merge_kernel<<<grid, block, 0, stream>>>(part, out, T, H, pos0, budget, KC);
+  merge_kernel<<<grid, block, 0, stream>>>(part, out, T, H, pos0, budget, KC, cpr);
   return hipGetLastError();
 }
 

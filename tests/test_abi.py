@@ -67,20 +67,28 @@ def test_flash_workspace_size():
     # 256 bytes).  T=512's blocks are at most 8 chunks: nothing is split.
     slot = (64 * 256 + 2 * 64) * 4
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=512, pos0=0)) == 2 * 8 * 65536
-    # up to 256 (token, group) rows above budget run as split records (the
-    # qsa_merge layout: 33 chunks x 24 heads x 258 floats per token) after
-    # the tiled part (rounded up to 256 bytes): T=200 at pos0 1900 tiles its
-    # 151 tokens under budget (29 blocks of 64 queries per group, 33 chunks
-    # each, in 3 pieces) and splits its 49 tokens above
-    rec = 33 * 24 * 258 * 4
+    # up to 256 (token, group) rows above budget run as row pieces after the
+    # tiled part (rounded up to 256 bytes): each piece covers cpr of a row's
+    # 33 chunks, cpr = ceil(rows x 33 / 1024) (about 1024 wavefronts), and
+    # writes one record per head (24 x 258 floats per piece and token).
+    # T=200 at pos0 1900 tiles its 151 tokens under budget (29 blocks of 64
+    # queries per group, 33 chunks each, in 3 pieces) and splits its 49
+    # tokens above (98 rows: cpr 4, 9 pieces per row)
+    def rec(tokens):
+        cpr = -(-tokens * 2 * 33 // 1024)
+        return tokens * -(-33 // cpr) * 24 * 258 * 4
     tile = 2 * 33 * 65536 + 256 + 3 * (2 * 29) * slot
+    assert rec(49) == 49 * 9 * 24 * 258 * 4
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=200, pos0=1900)) == \
-        (tile + 255) // 256 * 256 + 49 * rec
+        (tile + 255) // 256 * 256 + rec(49)
     # a call of at most 256 rows with some above budget splits every token
-    # (the budget-crossing chunk), and with none under budget as well; past
-    # 256 rows above budget the row kernel needs no workspace
-    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == 96 * rec
-    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=30000)) == 96 * rec
+    # (the budget-crossing chunk: 192 rows, cpr 7, 5 pieces per row), and
+    # with none under budget as well; past 256 rows above budget the row
+    # kernel needs no workspace
+    assert rec(96) == 96 * 5 * 24 * 258 * 4
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == rec(96)
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=30000)) == rec(96)
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=1, pos0=30000)) == 33 * 24 * 258 * 4
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=129, pos0=30000)) == 0
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=0, pos0=0)) == 0
 
