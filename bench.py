@@ -379,7 +379,7 @@ def roofline_of(r: dict, traffic) -> dict:
         kern = "qsa_flash: dequant_chunks_kernel + flash_tile_kernel<%d>" % (
             8 if 2 * -(-T * 12 // 128) >= 256 else 4)
     else:
-        kern = "qsa_flash: flash_rows_staged_kernel<false>"
+        kern = "qsa_flash: flash_rows_staged_kernel<false, false>"
     roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
             "traffic": traffic, "kernel": kern, "flops_per_launch": r["flops"],
