@@ -12,8 +12,10 @@
 // (token, group) row per wavefront and writes its (o, m, l) record (split
 // mode, the decode path).  flash_rows_staged_kernel (further down) attends a
 // whole row per wavefront, its gathers staged through LDS one stage ahead
-// (prompt tokens above budget).  Work mapping of the split kernel (gfx950,
-// wave64), shared in its PV half by the staged kernel:
+// (prompt tokens above budget), or, in its pieces form, a run of a row's
+// chunks per wavefront with one record per piece (calls with few rows, whose
+// rows alone would leave most SIMDs idle).  Work mapping of the split kernel
+// (gfx950, wave64), shared in its PV half by the staged kernel:
 //   * lane l: n = l % 16 is a query column (head n of the group, n < 12;
 //     columns 12..15 carry zero queries), j = l / 16 a k-slot group;
 //   * S^T[64 cells][16 queries] = K Q^T on v_mfma_f32_16x16x32_f16: A = K
