@@ -374,7 +374,7 @@ int qsa_flash_noalloc(const qsa_shape* s, const _Float16* q, const int8_t* kq,
   }
   const int64_t need = part ? 0 : min_workspace(s);
   if (need > QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_TOO_LARGE;
-  // the scratch holds the chunk images, and the split records of a route
+  // the scratch holds the chunk images, and the row-piece records of a route
   // that uses them when the route's whole workspace fits (with no token
   // under budget, only then is it needed)
   const int64_t full = part ? 0 : full_workspace(s);

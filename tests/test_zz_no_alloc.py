@@ -6,7 +6,7 @@ the scratch (both calls then take the same kernels), otherwise the same
 output within the oracle's bar (the scratch holds the chunk images, but a
 split route whose whole workspace it cannot hold leaves those rows to the
 row kernel); and the oracle's bar in every case.  The last pair has no
-token under budget: only the split records use the scratch."""
+token under budget: only the row-piece records use the scratch."""
 import numpy as np
 import pytest
 import torch
