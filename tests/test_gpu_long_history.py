@@ -6,7 +6,10 @@ kernels take their 64-bit addressing.  Only the cells some row selects are
 drawn (qsa_synth.sparse_history); the device arrays hold zeros elsewhere,
 so a gather from a wrong address shows up as a wrong output.  The oracle
 attends the same values from a compact copy (the selected cells renumbered
-in order), which changes no term of any row.
+in order), which changes no term of any row.  Three chunk sizes take the
+fused call's three row paths: 4 tokens (8 rows, one chunk per piece: the
+split kernel), 40 tokens (80 rows: row pieces of 3 chunks on the staged
+kernel) and 132 tokens (264 rows: the staged kernel, a row per wavefront).
 
 Selection: "sol_r6_qsa" (delivered change: the top-budget cells above
 budget); attention: "opus_r9_qsa" (what changed)."""
@@ -20,7 +23,6 @@ import quantized_sparse_flash_amd as qsa
 from gpu_util import DEV, Guarded, worst_row_rel_l2
 
 N_CELLS = (1 << 24) + 4096
-T = 4
 
 
 def _compact(h):
@@ -44,8 +46,9 @@ def _compact(h):
     return inp, ids
 
 
-@pytest.fixture(scope="module")
-def history():
+@pytest.fixture(scope="module", params=[4, 40, 132], ids=lambda t: "T%d" % t)
+def history(request):
+    T = request.param
     h = qsa_synth.sparse_history(T, N_CELLS - T, N_CELLS)
     assert int(h.ids.max()) >= (1 << 24)
     G = len(h.cells)
@@ -71,6 +74,7 @@ def history():
 @pytest.mark.gpu
 def test_fused_rows_past_2_24_cells(history):
     h, dev, ref = history
+    T = h.T
     s = qsa.QsaShape(T=T, pos0=h.pos0, n_groups=len(h.cells), budget=h.budget, n_cells=N_CELLS)
     out = Guarded((T, s.n_heads, 256), torch.float16, fill=float("nan"))
     qsa.qsa_flash(s, dev["q"], dev["kq"], dev["ksc"], dev["vq"], dev["vsc"], dev["ids"], out.t)
@@ -82,6 +86,7 @@ def test_fused_rows_past_2_24_cells(history):
 @pytest.mark.gpu
 def test_split_and_merge_past_2_24_cells(history):
     h, dev, ref = history
+    T = h.T
     s = qsa.QsaShape(T=T, pos0=h.pos0, n_groups=len(h.cells), budget=h.budget, n_cells=N_CELLS)
     part = Guarded((T, s.n_part_chunks, s.n_heads, qsa.PART_STRIDE), torch.float32,
                    fill=float("nan"))
