@@ -199,7 +199,7 @@ int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq
  * partial results through the workspace; it then also holds, per split
  * block, one partial of 64 x 258 floats per piece and a 4-byte counter
  * (the counters rounded up to 256 bytes).  qsa_flash_prepare clears the
- * counters; every call leaves them at zero.  When at most 256 (token,
+ * counters; every call leaves them at zero.  When at most 512 (token,
  * group) rows are above budget, they run as row pieces plus the merge,
  * which fill the GPU where one wavefront per row would not.  Each row is
  * cut into pieces of cpr consecutive 64-cell chunks of its selection,

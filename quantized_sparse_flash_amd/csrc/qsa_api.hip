@@ -52,26 +52,30 @@ int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUN
 // prefix of cells: the tiled path dequantises it once (the chunk images,
 // plus room for the split pieces of a tiled grid that leaves CUs idle) and
 // attends from it.  Rows above budget run on the row kernel, one wavefront
-// per row; when they are few (at most kRowsSplitMax) they run instead as
+// per row; when they are few (at most kRowPiecesMax) they run instead as
 // row pieces (one wavefront per piece of a few 64-cell chunks, about
 // kPieceWaves wavefronts in all) plus the merge, which fill the GPU where
 // a lone row would take the row kernel ~100 us.  Their records follow the
-// tiled part.  When the whole call has at most kRowsSplitMax rows and some
+// tiled part.  When the whole call has at most kAllPiecesMax rows and some
 // above budget, every token runs that way (the few tokens under budget
 // gain nothing from the tiled path's two extra launches), with the records
 // alone in the workspace.  The public calls
 // ask for the whole workspace of the route (qsa_flash_workspace_bytes);
 // qsa_flash_noalloc asks only for the chunk images, and takes a split
 // route only when its scratch holds that route's records.
-constexpr int64_t kRowsSplitMax = 256;  // (token, group) rows
+// (token, group) rows.  Measured at pos0 30000: pieces took 62 / 76 / 101
+// us for 300 / 400 / 600 rows against 104 us on the row kernel, and 130
+// against 106 us for 1000 rows (one piece per row: only the merge added).
+constexpr int64_t kRowPiecesMax = 512;
+constexpr int64_t kAllPiecesMax = 256;
 
 enum class Route { kRows, kSplitRows, kAllSplit };
 
 Route route_of(const qsa_shape* s) {
   const int64_t t_above = s->T - identity_tokens(s);
   if (t_above <= 0) return Route::kRows;  // no row above budget
-  if ((int64_t)s->T * s->n_groups <= kRowsSplitMax) return Route::kAllSplit;
-  if (t_above * s->n_groups <= kRowsSplitMax) return Route::kSplitRows;
+  if ((int64_t)s->T * s->n_groups <= kAllPiecesMax) return Route::kAllSplit;
+  if (t_above * s->n_groups <= kRowPiecesMax) return Route::kSplitRows;
   return Route::kRows;
 }
 // Chunks per record of the row pieces of `rows` (token, group) rows: about

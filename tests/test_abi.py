@@ -67,7 +67,7 @@ def test_flash_workspace_size():
     # 256 bytes).  T=512's blocks are at most 8 chunks: nothing is split.
     slot = (64 * 256 + 2 * 64) * 4
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=512, pos0=0)) == 2 * 8 * 65536
-    # up to 256 (token, group) rows above budget run as row pieces after the
+    # up to 512 (token, group) rows above budget run as row pieces after the
     # tiled part (rounded up to 256 bytes): each piece covers cpr of a row's
     # 33 chunks, cpr = ceil(rows x 33 / 1024) (about 1024 wavefronts), and
     # writes one record per head (24 x 258 floats per piece and token).
@@ -83,13 +83,16 @@ def test_flash_workspace_size():
         (tile + 255) // 256 * 256 + rec(49)
     # a call of at most 256 rows with some above budget splits every token
     # (the budget-crossing chunk: 192 rows, cpr 7, 5 pieces per row), and
-    # with none under budget as well; past 256 rows above budget the row
+    # with none under budget as well; up to 512 rows above budget run as
+    # pieces (258 rows: cpr 9, 4 pieces per row); past 512 rows the row
     # kernel needs no workspace
     assert rec(96) == 96 * 5 * 24 * 258 * 4
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=2050)) == rec(96)
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=96, pos0=30000)) == rec(96)
+    assert rec(129) == 129 * 4 * 24 * 258 * 4
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=129, pos0=30000)) == rec(129)
+    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=257, pos0=30000)) == 0
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=1, pos0=30000)) == 33 * 24 * 258 * 4
-    assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=129, pos0=30000)) == 0
     assert qsa.qsa_flash_workspace_bytes(qsa.QsaShape(T=0, pos0=0)) == 0
 
 

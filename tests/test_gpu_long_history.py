@@ -9,7 +9,7 @@ attends the same values from a compact copy (the selected cells renumbered
 in order), which changes no term of any row.  Three chunk sizes take the
 fused call's three row paths: 4 tokens (8 rows, one chunk per piece: the
 split kernel), 40 tokens (80 rows: row pieces of 3 chunks on the staged
-kernel) and 132 tokens (264 rows: the staged kernel, a row per wavefront).
+kernel) and 260 tokens (520 rows: the staged kernel, a row per wavefront).
 
 Selection: "sol_r6_qsa" (delivered change: the top-budget cells above
 budget); attention: "opus_r9_qsa" (what changed)."""
@@ -46,7 +46,7 @@ def _compact(h):
     return inp, ids
 
 
-@pytest.fixture(scope="module", params=[4, 40, 132], ids=lambda t: "T%d" % t)
+@pytest.fixture(scope="module", params=[4, 40, 260], ids=lambda t: "T%d" % t)
 def history(request):
     T = request.param
     h = qsa_synth.sparse_history(T, N_CELLS - T, N_CELLS)
