@@ -25,6 +25,9 @@ Other workloads (--workload):
                                   decode8_pos30000);
   t1984_pos30000_split            the long-context prompt through the same
                                   split path instead of the fused one;
+  t96_pos2050, t32_pos2050,       one layer of qsa_topk + qsa_flash whose
+  t200_pos1900, t200_pos30000     rows above budget are few enough to run
+                                  as row pieces plus the merge;
   quantize_kv_31984               the K/V quantiser on the long-context
                                   cache (cells quantised per second);
   score_t1984_pos30000            the selection scores of the long-context
@@ -93,6 +96,12 @@ WORKLOADS = {
     "decode8_pos2048": dict(T=8, pos0=2048, layers=1, kind="split"),
     "decode8_pos30000": dict(T=8, pos0=30000, layers=1, kind="split"),
     "t1984_pos30000_split": dict(T=1984, pos0=30000, layers=1, kind="split"),
+    # fused calls with few rows above budget (row pieces): the budget-crossing
+    # chunks, a crossing after 151 tiled tokens, and 400 rows at long context
+    "t96_pos2050": dict(T=96, pos0=2050, layers=1, kind="prompt"),
+    "t32_pos2050": dict(T=32, pos0=2050, layers=1, kind="prompt"),
+    "t200_pos1900": dict(T=200, pos0=1900, layers=1, kind="prompt"),
+    "t200_pos30000": dict(T=200, pos0=30000, layers=1, kind="prompt"),
     "quantize_kv_31984": dict(T=1984, pos0=30000, layers=1, kind="quantize"),
     "score_t1984_pos30000": dict(T=1984, pos0=30000, layers=1, kind="score"),
 }
@@ -366,6 +375,27 @@ def measure(workload: str, args, dev, flush) -> dict:
     return res
 
 
+def fused_kernels(T: int, pos0: int, budget: int, G: int = 2) -> str:
+    """The kernels a fused qsa_flash call of this shape enqueues, for the
+    bench line's label (the library's routing: tokens under budget on the
+    tiled path; rows above budget as row pieces plus the merge when at most
+    512 of them, every token so when the call has at most 256 rows, else
+    one wavefront per row)."""
+    t_id = max(0, min(T, budget - pos0))
+    rows_above = (T - t_id) * G
+    # 8-wave tiles of 128 queries when at least 256 of them cover the tokens
+    tiled = "dequant_chunks_kernel + flash_tile_kernel<%d>" % (
+        8 if G * -(-t_id * 12 // 128) >= 256 else 4)
+    pieces = ("row pieces (flash_rows_staged_kernel<false, true>, or flash_split_kernel "
+              "when each piece is one chunk) + merge_kernel")
+    if rows_above == 0:
+        return tiled
+    if T * G <= 256:
+        return pieces
+    rest = pieces if rows_above <= 512 else "flash_rows_staged_kernel<false, false>"
+    return tiled + " + " + rest if t_id else rest
+
+
 def roofline_of(r: dict, traffic) -> dict:
     """The roofline object of a measured workload (see the module text)."""
     T, pos0, kind = r["T"], r["pos0"], r["kind"]
@@ -373,13 +403,8 @@ def roofline_of(r: dict, traffic) -> dict:
     identity = pos0 + T <= r["budget"]
     if kind == "split":
         kern = "qsa_flash in split mode: flash_split_kernel"
-    elif identity:
-        # 8-wave workgroups of 128 queries when at least 256 of them cover
-        # the prompt (2 groups), else 4-wave ones of 64
-        kern = "qsa_flash: dequant_chunks_kernel + flash_tile_kernel<%d>" % (
-            8 if 2 * -(-T * 12 // 128) >= 256 else 4)
     else:
-        kern = "qsa_flash: flash_rows_staged_kernel<false, false>"
+        kern = "qsa_flash: " + fused_kernels(T, pos0, r["budget"])
     roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
             "traffic": traffic, "kernel": kern, "flops_per_launch": r["flops"],

@@ -61,3 +61,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_fused_kernel_labels_follow_the_routes():
+    assert bench.fused_kernels(1984, 0, 2051) == \
+        "dequant_chunks_kernel + flash_tile_kernel<8>"
+    assert bench.fused_kernels(512, 0, 2051) == \
+        "dequant_chunks_kernel + flash_tile_kernel<4>"
+    # at most 256 rows: every token as row pieces
+    assert bench.fused_kernels(96, 2050, 2051).startswith("row pieces")
+    # tokens under budget tiled, up to 512 rows above as pieces, else a row
+    # per wavefront
+    assert bench.fused_kernels(200, 1900, 2051) == \
+        "dequant_chunks_kernel + flash_tile_kernel<4> + " + bench.fused_kernels(96, 2050, 2051)
+    assert bench.fused_kernels(200, 30000, 2051).startswith("row pieces")
+    assert bench.fused_kernels(1984, 30000, 2051) == "flash_rows_staged_kernel<false, false>"
