@@ -59,23 +59,25 @@ int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUN
 // tiled part.  When the whole call has at most kAllPiecesMax rows and some
 // above budget, every token runs that way (the few tokens under budget
 // gain nothing from the tiled path's two extra launches), with the records
-// alone in the workspace.  The public calls
-// ask for the whole workspace of the route (qsa_flash_workspace_bytes);
-// qsa_flash_noalloc asks only for the chunk images, and takes a split
-// route only when its scratch holds that route's records.
-// (token, group) rows.  Measured at pos0 30000: pieces took 62 / 76 / 101
-// us for 300 / 400 / 600 rows against 104 us on the row kernel, and 130
-// against 106 us for 1000 rows (one piece per row: only the merge added).
+// alone in the workspace.  The public calls ask for the whole workspace of
+// the route (qsa_flash_workspace_bytes); qsa_flash_noalloc asks only for
+// the chunk images, and takes a pieces route only when its scratch holds
+// that route's records.
+//
+// Both limits count (token, group) rows.  Measured at pos0 30000: pieces
+// took 62 / 76 / 101 us for 300 / 400 / 600 rows against 104 us on the row
+// kernel, and 130 against 106 us for 1000 rows (one piece per row: only
+// the merge added).
 constexpr int64_t kRowPiecesMax = 512;
 constexpr int64_t kAllPiecesMax = 256;
 
-enum class Route { kRows, kSplitRows, kAllSplit };
+enum class Route { kRows, kRowPieces, kAllPieces };
 
 Route route_of(const qsa_shape* s) {
   const int64_t t_above = s->T - identity_tokens(s);
   if (t_above <= 0) return Route::kRows;  // no row above budget
-  if ((int64_t)s->T * s->n_groups <= kAllPiecesMax) return Route::kAllSplit;
-  if (t_above * s->n_groups <= kRowPiecesMax) return Route::kSplitRows;
+  if ((int64_t)s->T * s->n_groups <= kAllPiecesMax) return Route::kAllPieces;
+  if (t_above * s->n_groups <= kRowPiecesMax) return Route::kRowPieces;
   return Route::kRows;
 }
 // Chunks per record of the row pieces of `rows` (token, group) rows: about
@@ -99,12 +101,12 @@ int64_t tile_part_bytes(const qsa_shape* s) {
 }
 int64_t full_workspace(const qsa_shape* s) {
   switch (route_of(s)) {
-    case Route::kAllSplit: return record_bytes(s, s->T);
-    case Route::kSplitRows: return tile_part_bytes(s) + record_bytes(s, s->T - identity_tokens(s));
+    case Route::kAllPieces: return record_bytes(s, s->T);
+    case Route::kRowPieces: return tile_part_bytes(s) + record_bytes(s, s->T - identity_tokens(s));
     default: return qsa::tile_workspace_bytes(s->n_groups, identity_tokens(s), s->pos0);
   }
 }
-// The route a call with workspace_bytes of scratch takes: a split route
+// The route a call with workspace_bytes of scratch takes: a pieces route
 // only when the scratch holds its workspace.
 Route route_with(const qsa_shape* s, int64_t workspace_bytes) {
   const Route r = route_of(s);
@@ -220,7 +222,7 @@ int prepare_impl(const qsa_shape* s, const int8_t* kq, const _Float16* ksc, cons
   int rc = flash_args(s, nullptr, kq, ksc, vq, vsc, nullptr, nullptr, nullptr, &a);
   if (rc == QSA_OK) rc = check_workspace(workspace, workspace_bytes, need);
   if (rc != QSA_OK) return rc;
-  if (route_with(s, workspace_bytes) == Route::kAllSplit) return QSA_OK;  // nothing to prepare
+  if (route_with(s, workspace_bytes) == Route::kAllPieces) return QSA_OK;  // nothing to prepare
   return launch_status(qsa::launch_tile_prepare(a, identity_tokens(s), workspace,
                                                 workspace_bytes, (hipStream_t)stream));
 }
@@ -241,7 +243,7 @@ int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _
   hipStream_t st = (hipStream_t)stream;
   // tokens [t0, T) as a shape of their own: row-piece records in the
   // workspace from byte `off`, then the merge into out
-  auto split_tokens = [&](int t0, int64_t off) {
+  auto piece_tokens = [&](int t0, int64_t off) {
     qsa::RowArgs b = a;
     b.q = a.q + (int64_t)t0 * H * QSA_HEAD_DIM;
     b.out = a.out + (int64_t)t0 * H * QSA_HEAD_DIM;
@@ -259,10 +261,10 @@ int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _
         qsa::launch_merge(b.part, b.out, b.T, (int)H, b.pos0, s->budget, b.cpr, st));
   };
   const Route route = route_with(s, workspace_bytes);
-  if (route == Route::kAllSplit) return split_tokens(0, 0);
+  if (route == Route::kAllPieces) return piece_tokens(0, 0);
   rc = launch_status(qsa::launch_tile_attend(a, t_id, workspace, workspace_bytes, st));
   if (rc != QSA_OK) return rc;
-  if (route == Route::kSplitRows) return split_tokens(t_id, tile_part_bytes(s));
+  if (route == Route::kRowPieces) return piece_tokens(t_id, tile_part_bytes(s));
   return launch_status(qsa::launch_flash_rows(a, false, t_id, st));
 }
 
