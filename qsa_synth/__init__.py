@@ -15,8 +15,8 @@ Workload shapes follow the pages (quantized_sparse_flash audits):
 
 The value distributions (queries N(0,1) as fp16, codes uniform in
 [-127, 127], scales uniform in [0.002, 0.02], selection scores N(0,1) fp32)
-are this build's stated recipe: the pages name the kinds of inputs but not
-their distributions.
+are a chosen recipe: the pages name the kinds of inputs but not their
+distributions.
 
 Generator: numpy PCG64 seeded with the tuple (seed, T, pos0, layer); draws
 happen in a fixed order (q, kq, ksc, vq, vsc, scores) so that adding the
@@ -158,8 +158,8 @@ def sparse_history(T: int, pos0: int, n_cells: int, seed: int = SEED, *, budget:
 def score_inputs(T: int, pos0: int, index_dim: int = 4, seed: int = SEED, *,
                  n_groups: int = N_GROUPS, n_cells: Optional[int] = None) -> tuple:
     """Inputs of the selection-score step: qidx [T][G][index_dim] and pooled
-    [G][n_cells][index_dim], both N(0,1) fp32 (this build's recipe; the
-    pages name the buffers, not their distributions)."""
+    [G][n_cells][index_dim], both N(0,1) fp32 (a chosen recipe; the pages
+    name the buffers, not their distributions)."""
     if n_cells is None:
         n_cells = pos0 + T
     rng = np.random.default_rng([seed, T, pos0, index_dim, 43])
