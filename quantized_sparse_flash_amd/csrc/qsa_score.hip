@@ -24,7 +24,11 @@
 //     steps of four values.
 // Only rows above budget are written (their top-k reads them).  At the
 // long-context shape the kernels write ~0.5 GB of scores: they are bound by
-// those HBM writes.
+// those HBM writes.  The stores are non-temporal: 0.5 GB does not fit the
+// Infinity Cache, and scores written through it left dirty lines whose
+// write-back met the top-k's reads (score then top-k at T=1984, pos0 30000:
+// 246-277 against 261-297 us; the score kernel alone 102-105 against
+// 107-108 us).
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -74,7 +78,7 @@ void score_kernel(const float* __restrict__ qidx, const float* __restrict__ pool
 #pragma unroll
     for (int k = 0; k < kScorePasses; ++k) {
       const int64_t c = base + (int64_t)kScoreThreads * k;
-      if (c < nkv) out[c] = acc[k];
+      if (c < nkv) __builtin_nontemporal_store(acc[k], out + c);
     }
   }
 }
@@ -130,11 +134,12 @@ void score4_kernel(const float* __restrict__ qidx, const float* __restrict__ poo
       }
       const int64_t c0 = base + 1024 * p;
       if (vec_store && c0 + 4 <= nkv) {
-        *reinterpret_cast<f32x4_t*>(out + c0) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+        __builtin_nontemporal_store(f32x4_t{acc[0], acc[1], acc[2], acc[3]},
+                                    reinterpret_cast<f32x4_t*>(out + c0));
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (c0 + e < nkv) out[c0 + e] = acc[e];
+          if (c0 + e < nkv) __builtin_nontemporal_store(acc[e], out + c0 + e);
       }
     }
   }
