@@ -483,6 +483,7 @@ constexpr int kListThreads = 512;
 constexpr int kListEpt = 64;     // slices: rows up to 32,768 cells
 constexpr int kListBatch = 16;   // slices in flight per thread
 constexpr int kListPairs = 4608; // (key, cell) pairs the list holds
+constexpr int kCachePolicyNt = 2;  // buffer-load cache policy: non-temporal (nt)
 
 template <int EPT>
 __global__ __launch_bounds__(kListThreads) __attribute__((amdgpu_waves_per_eu(8))) void
@@ -520,6 +521,19 @@ topk_list_kernel(const float* __restrict__ scores, int32_t* __restrict__ ids, in
         (void*)(srow + start), (short)0, 4 * (n32 - start), kBufferFlags);
     return __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 0, 0);
   };
+  // the same load, non-temporal (cache policy nt), for the stream: each
+  // score is read once there, and 0.5 GB of them no longer sweep the KV
+  // cells that the attention launch after the top-k gathers out of the
+  // Infinity Cache (long-context step 0.420 against 0.421 ms back to back,
+  // single steps after a cache flush 0.455-0.481 against 0.499-0.509 ms).
+  // The sample keeps the ordinary load: the stream reads those cells again
+  // and finds them in L2.
+  auto load_slice_nt = [&](int i) -> uint32_t {
+    const int start = min(NT * i, n32);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(srow + start), (short)0, 4 * (n32 - start), kBufferFlags);
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 0, kCachePolicyNt);
+  };
   // its key, 0 past the row's end (below every score)
   auto key_of = [&](uint32_t bits, int i) -> uint32_t {
     const uint32_t k = score_key(__builtin_bit_cast(float, bits));
@@ -544,7 +558,7 @@ topk_list_kernel(const float* __restrict__ scores, int32_t* __restrict__ ids, in
   // the sample picks the threshold
   uint32_t k[kListBatch];
 #pragma unroll
-  for (int j = 0; j < kListBatch; ++j) k[j] = load_slice(j);
+  for (int j = 0; j < kListBatch; ++j) k[j] = load_slice_nt(j);
   {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(&hist[4 * tid]) = zero;
@@ -584,7 +598,7 @@ topk_list_kernel(const float* __restrict__ scores, int32_t* __restrict__ ids, in
   for (int b = 0; b < EPT; b += kListBatch) {
     if (b > 0) {
 #pragma unroll
-      for (int j = 0; j < kListBatch; ++j) k[j] = load_slice(b + j);
+      for (int j = 0; j < kListBatch; ++j) k[j] = load_slice_nt(b + j);
     }
     uint32_t off[kListBatch];  // hits of the wave's earlier slices, plus the lane's rank
     uint32_t run = 0;
