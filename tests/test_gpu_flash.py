@@ -197,12 +197,14 @@ def test_maximum_budget():
     _check(gpu_merge(inp, part), ref)
 
 
-@pytest.mark.parametrize("G", [1, 3, 4])
-@pytest.mark.parametrize("T,pos0", [(70, 0), (40, 2030), (6, 5000)])
+@pytest.mark.parametrize("G", [1, 3, 4, 8])
+@pytest.mark.parametrize("T,pos0", [(70, 0), (40, 2030), (6, 5000), (70, 3000)])
 def test_other_group_counts(G, T, pos0):
     # 12 heads per group, G groups: the tile kernel's group interleave, the
-    # row kernel's per-XCD group mapping (G dividing the 8 XCDs) and its
-    # plain mapping (G = 3), selection and split + merge
+    # row pieces, the row kernel's per-XCD group mapping with one XCD per
+    # group (G = 8, whose 560 rows above budget at (70, 3000) take the row
+    # kernel; G = 3, which does not divide the 8 XCDs, reaches it in the
+    # random-shape test), selection and split + merge
     inp = qsa_synth.layer_inputs(T, pos0, seed=G * 100 + T, n_groups=G)
     ids = None
     dev = upload(inp)
