@@ -3,22 +3,25 @@
  * path.  TEST INFRASTRUCTURE ONLY: nothing in the product path may call it.
  * It shares no code, header or constant with the HIP library.
  *
- * What the path computes, per prompt token t and KV group g (pages:
- * quantized_sparse_flash audits "sol_r6_qsa" and "opus_r9_qsa"):
+ * What the path computes, per prompt token t and KV group g (pages
+ * "round 6 track b - qsa flash" and "opus_r9_qsa"):
  *   1. the token sees n = pos0 + t + 1 KV cells (itself included);
  *   2. selection: every cell when n <= budget ("identity ids"), otherwise the
  *      `budget` cells with the largest selection score, ties to the lower
- *      index, listed in ascending order ("sol_r6_qsa", delivered change;
- *      "selected-index semantics above budget");
+ *      index, listed in ascending order ("round 6 track b - qsa flash",
+ *      delivered change; experiment contract: selected-index semantics
+ *      above budget);
  *   3. for each of the group's query heads h: s_c = 0.0625 * q_h . k_c with
  *      k_c[d] = kq[c][d] * ksc[c][d/64] ("opus_r9_qsa", what changed: the
- *      *0.0625f combine; "sol_r6_qsa", delivered change: half4 scales);
+ *      0.0625 combine; "round 6 track b - qsa flash", delivered change: four
+ *      scales per cell);
  *   4. softmax over the selected cells and o = sum_c w_c v_c with
  *      v_c[d] = vq[c][d] * vsc[c][d/64].
  * The chunked online softmax and the (m, l) log-sum-exp merge of the pages
- * ("sol_r27_qsa", decision and correctness) are a faster route to the same
- * number; the oracle states the plain definition and, separately, the
- * chunk-partial and merge steps so that their invariants can be checked.
+ * ("round 27 track b - qsa prep and merge", decision and correctness) are a
+ * faster route to the same number; the oracle states the plain definition
+ * and, separately, the chunk-partial and merge steps so that their
+ * invariants can be checked.
  *
  * Everything is fp64.  fp16 inputs are widened by the caller (exact).
  */
@@ -50,10 +53,10 @@ static int by_int_asc(const void *pa, const void *pb) {
 }
 
 /* Selection scores.  The pages name the score kernel and its buffers
- * ("sol_r27_qsa", decision: four-value dot products; correctness: qidx,
- * pooled, scores) but not their content; the reading taken: the score of
- * cell c for token t in group g is the dot product of the token's index
- * query with the cell's pooled key,
+ * ("round 27 track b - qsa prep and merge", decision: four-value dot
+ * products; correctness: qidx, pooled, scores) but not their content; the
+ * reading taken: the score of cell c for token t in group g is the dot
+ * product of the token's index query with the cell's pooled key,
  *   scores[t][g][c] = sum_d qidx[t][g][d] * pooled[g][c][d],
  * written for the rows above budget (n > budget, the rows whose selection
  * reads scores) at cells c < n; every other element is left as it was.
@@ -259,8 +262,8 @@ int qsa_oracle_partials(int T, int pos0, int G, int HPG, int D, int budget, int6
   return bad ? ORACLE_BAD : ORACLE_OK;
 }
 
-/* Log-sum-exp merge of chunk partials ("sol_r27_qsa", decision: the (m, l)
- * merge of chunk partials).  part is the fp32 record layout of the split
+/* Log-sum-exp merge of chunk partials ("round 27 track b - qsa prep and
+ * merge", decision: the (m, l) merge of chunk partials).  part is the fp32 record layout of the split
  * form: part[((t*KC + k)*H + h)*(D+2) + 0..D-1] = o_k (unnormalised),
  * [+D] = m_k, [+D+1] = l_k.  nchunks[t] chunks are merged for token t:
  *   M = max_k m_k,  L = sum_k l_k e^{m_k - M},  out = sum_k e^{m_k - M} o_k / L.
@@ -295,8 +298,8 @@ int qsa_oracle_merge(int T, int H, int D, int KC, const int32_t *nchunks, const 
 
 /* ------------------------------------------------------------------------
  * K/V quantiser: the step that fills the int8 cache the path reads (the
- * quantiser part of the pages' prep step; "sol_r6_qsa", delivered change:
- * int8 codes with one fp16 scale per 64 dims).  The pages do not state the
+ * quantiser part of the pages' prep step; "round 6 track b - qsa flash",
+ * delivered change: int8 codes with one fp16 scale per 64 dims).  The pages do not state the
  * rounding rule; the reading taken is the plain absmax one, per row and
  * 64-dim block b:
  *   amax  = max_d |x[d]|                        (exact)

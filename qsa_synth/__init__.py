@@ -5,13 +5,16 @@ arithmetic.  Both the fp64 oracle (``oracle/``) and the HIP path
 (``quantized_sparse_flash_amd``) are fed from here, so their inputs are
 identical bit for bit.
 
-Workload shapes follow the pages (quantized_sparse_flash audits):
-  * 2 KV groups x 12 query heads, head dim 256 ("sol_r6_qsa", experiment
-    contract and delivered change; "opus_r9_qsa", what changed: HPG x QCH);
+Workload shapes follow the pages:
+  * 2 KV groups x 12 query heads, head dim 256 ("round 6 track b - qsa
+    flash", experiment contract and delivered change; "opus_r9_qsa", what
+    changed: HPG x QCH);
   * int8 K/V codes with one fp16 scale per 64 dims (a half4 per cell)
-    ("sol_r6_qsa", delivered change);
-  * deterministic random inputs from rng seed 5 ("sol_r6_qsa", actual runs);
-  * a 2051-cell selection budget ("sol_r6_qsa", delivered change).
+    ("round 6 track b - qsa flash", delivered change);
+  * deterministic random inputs from rng seed 5 ("round 6 track b - qsa
+    flash", actual runs);
+  * a 2051-cell selection budget ("round 6 track b - qsa flash", delivered
+    change).
 
 The value distributions (queries N(0,1) as fp16, codes uniform in
 [-127, 127], scales uniform in [0.002, 0.02], selection scores N(0,1) fp32)

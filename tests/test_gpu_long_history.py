@@ -11,8 +11,9 @@ fused call's three row paths: 4 tokens (8 rows, one chunk per piece: the
 split kernel), 40 tokens (80 rows: row pieces of 3 chunks on the staged
 kernel) and 260 tokens (520 rows: the staged kernel, a row per wavefront).
 
-Selection: "sol_r6_qsa" (delivered change: the top-budget cells above
-budget); attention: "opus_r9_qsa" (what changed)."""
+Selection: page "round 6 track b - qsa flash" (delivered change: the
+top-budget cells above budget); attention: page "opus_r9_qsa" (what
+changed)."""
 import numpy as np
 import pytest
 import torch

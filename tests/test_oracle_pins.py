@@ -258,7 +258,8 @@ def test_partials_chunk_max_and_sum_definitions():
             assert l[0, kk, h] == pytest.approx(np.exp(blk - blk.max()).sum(), rel=1e-13)
 
 
-# ---- selection scores (the reading of "sol_r27_qsa": qidx . pooled per cell)
+# ---- selection scores (the reading of "round 27 track b - qsa prep
+# and merge": qidx . pooled per cell)
 
 def test_score_agrees_with_a_python_sum():
     """Every score of the rows above budget equals the dot product summed
