@@ -35,6 +35,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qsa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libqsa_oracle.so")
+# Set only by tests/test_oracle_mutants.py, in the child processes it starts:
+# a build of qsa_oracle.c with one planted mistake, which the pins must reject.
+_MUTANT_ENV = "QSA_ORACLE_MUTANT_LIB"
 _lib = None
 
 
@@ -54,9 +57,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB_PATH)
+    path = os.environ.get(_MUTANT_ENV)
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build(force=True)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.qsa_oracle_select.argtypes = [i32, i32, i32, i32, i64, P, P]
