@@ -57,6 +57,19 @@ def test_budget_crossing_chunk(T, pos0):
     _check(gpu_flash(inp, gids, dev), ref)
 
 
+@pytest.mark.parametrize("T,pos0", [(150, 30000), (200, 30000), (400, 1900)])
+def test_row_piece_workloads(T, pos0):
+    # 300 to 498 rows above budget, the benchmark's row-piece shapes: pieces
+    # of 10, 13 and 17 chunks at long context and after 151 tiled tokens,
+    # with their merge; the benchmark's layer-0 inputs, ids from qsa_topk
+    inp = qsa_synth.layer_inputs(T, pos0, layer=0)
+    ids = oracle.select(T, pos0, inp.budget, inp.scores, 2, inp.n_cells)
+    dev = upload(inp)
+    gids = gpu_topk(inp, dev)
+    np.testing.assert_array_equal(gids, ids)
+    _check(gpu_flash(inp, gids, dev), oracle.attend(inp, ids))
+
+
 def test_poisoned_ids_are_not_read_under_budget():
     # crossing chunk: token 0 is under budget; its ids are poisoned to -1 and
     # identity rows of a fully-under-budget chunk get ids=NULL vs all -1
