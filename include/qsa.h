@@ -61,6 +61,12 @@ extern "C" {
 #define QSA_DEFAULT_BUDGET 2051
 #define QSA_NOALLOC_SCRATCH_BYTES (16 << 20) /* device scratch held by qsa_flash_noalloc */
 
+/* An fp16 element: the IEEE 754 binary16 bit pattern, two bytes.  The
+ * library only hands these pointers to the GPU, so the host-side element
+ * type is a plain 16-bit integer that every C and C++ compiler has; a
+ * caller's _Float16 or __half array is passed with a pointer cast. */
+typedef uint16_t qsa_f16;
+
 /* Shape of one prompt chunk of one layer. */
 typedef struct {
   int32_t T;               /* query tokens in the chunk, >= 1 */
@@ -158,8 +164,8 @@ int qsa_topk(const qsa_shape *shape, const float *scores, int32_t *ids, void *st
  * that each piece is one chunk); relative L2 error against exact attention
  * about 4e-4 on the pages' value ranges.
  */
-int qsa_flash(const qsa_shape *shape, const _Float16 *q, const int8_t *kq, const _Float16 *ksc,
-              const int8_t *vq, const _Float16 *vsc, const int32_t *ids, _Float16 *out,
+int qsa_flash(const qsa_shape *shape, const qsa_f16 *q, const int8_t *kq, const qsa_f16 *ksc,
+              const int8_t *vq, const qsa_f16 *vsc, const int32_t *ids, qsa_f16 *out,
               float *part, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
@@ -178,12 +184,12 @@ int qsa_flash(const qsa_shape *shape, const _Float16 *q, const int8_t *kq, const
  * written by qsa_flash_attend.  Attending without a prepared workspace
  * gives unspecified output values (never an out-of-bounds access).
  */
-int qsa_flash_prepare(const qsa_shape *shape, const int8_t *kq, const _Float16 *ksc,
-                      const int8_t *vq, const _Float16 *vsc, void *workspace,
+int qsa_flash_prepare(const qsa_shape *shape, const int8_t *kq, const qsa_f16 *ksc,
+                      const int8_t *vq, const qsa_f16 *vsc, void *workspace,
                       int64_t workspace_bytes, void *stream);
-int qsa_flash_attend(const qsa_shape *shape, const _Float16 *q, const int8_t *kq,
-                     const _Float16 *ksc, const int8_t *vq, const _Float16 *vsc,
-                     const int32_t *ids, _Float16 *out, void *workspace,
+int qsa_flash_attend(const qsa_shape *shape, const qsa_f16 *q, const int8_t *kq,
+                     const qsa_f16 *ksc, const int8_t *vq, const qsa_f16 *vsc,
+                     const int32_t *ids, qsa_f16 *out, void *workspace,
                      int64_t workspace_bytes, void *stream);
 
 /*
@@ -238,9 +244,9 @@ int64_t qsa_flash_workspace_bytes(const qsa_shape *shape);
  *   whole, and on the row kernel otherwise.  Either difference changes the
  *   output only by rounding.
  */
-int qsa_flash_noalloc(const qsa_shape *shape, const _Float16 *q, const int8_t *kq,
-                      const _Float16 *ksc, const int8_t *vq, const _Float16 *vsc,
-                      const int32_t *ids, _Float16 *out, float *part, void *stream);
+int qsa_flash_noalloc(const qsa_shape *shape, const qsa_f16 *q, const int8_t *kq,
+                      const qsa_f16 *ksc, const int8_t *vq, const qsa_f16 *vsc,
+                      const int32_t *ids, qsa_f16 *out, float *part, void *stream);
 
 /*
  * qsa_merge -- log-sum-exp merge of split-mode partials (page "round 27
@@ -252,7 +258,7 @@ int qsa_flash_noalloc(const qsa_shape *shape, const _Float16 *q, const int8_t *k
  *   out  : device, fp16 [T][G*12][256].
  * Alignment: 16 bytes for both.
  */
-int qsa_merge(const qsa_shape *shape, const float *part, _Float16 *out, void *stream);
+int qsa_merge(const qsa_shape *shape, const float *part, qsa_f16 *out, void *stream);
 
 /*
  * qsa_quantize -- the K/V quantiser that fills the int8 cache (the prep step
@@ -274,8 +280,8 @@ int qsa_merge(const qsa_shape *shape, const float *part, _Float16 *out, void *st
  * QSA_ERR_UNSUPPORTED (dim), QSA_ERR_SHAPE (n_rows < 0 or too large),
  * QSA_ERR_ARG (NULL or misaligned pointer).
  */
-int qsa_quantize(int64_t n_rows, int32_t dim, const _Float16 *x, int8_t *codes,
-                 _Float16 *scales, void *stream);
+int qsa_quantize(int64_t n_rows, int32_t dim, const qsa_f16 *x, int8_t *codes,
+                 qsa_f16 *scales, void *stream);
 
 /* Human-readable text of a status code (static storage). */
 const char *qsa_status_string(int status);

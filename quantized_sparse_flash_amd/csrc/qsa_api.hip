@@ -174,21 +174,21 @@ int64_t qsa_flash_workspace_bytes(const qsa_shape* s) {
 namespace {
 
 // Host-side checks and argument packing shared by the qsa_flash entry points.
-int flash_args(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
-               const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+int flash_args(const qsa_shape* s, const qsa_f16* q, const int8_t* kq, const qsa_f16* ksc,
+               const int8_t* vq, const qsa_f16* vsc, const int32_t* ids, qsa_f16* out,
                float* part, qsa::RowArgs* a) {
   int rc = check_shape(s);
   if (rc != QSA_OK) return rc;
   if (!kq || !ksc || !vq || !vsc) return QSA_ERR_ARG;
   if (!aligned(kq, 16) || !aligned(vq, 16) || !aligned(ksc, 8) || !aligned(vsc, 8))
     return QSA_ERR_ARG;
-  a->q = q;
+  a->q = reinterpret_cast<const _Float16*>(q);
   a->kq = kq;
-  a->ksc = ksc;
+  a->ksc = reinterpret_cast<const _Float16*>(ksc);
   a->vq = vq;
-  a->vsc = vsc;
+  a->vsc = reinterpret_cast<const _Float16*>(vsc);
   a->ids = ids;
-  a->out = out;
+  a->out = reinterpret_cast<_Float16*>(out);
   a->part = part;
   a->T = s->T;
   a->pos0 = s->pos0;
@@ -208,15 +208,15 @@ int check_workspace(const void* workspace, int64_t workspace_bytes, int64_t need
 }
 
 // q, ids and out of a fused call (attention half).
-int check_attend(const qsa_shape* s, const _Float16* q, const int32_t* ids, const _Float16* out) {
+int check_attend(const qsa_shape* s, const qsa_f16* q, const int32_t* ids, const qsa_f16* out) {
   if (!q || !aligned(q, 16)) return QSA_ERR_ARG;
   if (any_above_budget(s) && (!ids || !aligned(ids, 4))) return QSA_ERR_ARG;
   if (!out || !aligned(out, 16)) return QSA_ERR_ARG;
   return QSA_OK;
 }
 
-int prepare_impl(const qsa_shape* s, const int8_t* kq, const _Float16* ksc, const int8_t* vq,
-                 const _Float16* vsc, void* workspace, int64_t workspace_bytes, void* stream,
+int prepare_impl(const qsa_shape* s, const int8_t* kq, const qsa_f16* ksc, const int8_t* vq,
+                 const qsa_f16* vsc, void* workspace, int64_t workspace_bytes, void* stream,
                  int64_t need) {
   qsa::RowArgs a;
   int rc = flash_args(s, nullptr, kq, ksc, vq, vsc, nullptr, nullptr, nullptr, &a);
@@ -227,8 +227,8 @@ int prepare_impl(const qsa_shape* s, const int8_t* kq, const _Float16* ksc, cons
                                                 workspace_bytes, (hipStream_t)stream));
 }
 
-int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
-                const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+int attend_impl(const qsa_shape* s, const qsa_f16* q, const int8_t* kq, const qsa_f16* ksc,
+                const int8_t* vq, const qsa_f16* vsc, const int32_t* ids, qsa_f16* out,
                 void* workspace, int64_t workspace_bytes, void* stream, int64_t need) {
   qsa::RowArgs a;
   int rc = flash_args(s, q, kq, ksc, vq, vsc, ids, out, nullptr, &a);
@@ -268,8 +268,8 @@ int attend_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _
   return launch_status(qsa::launch_flash_rows(a, false, t_id, st));
 }
 
-int flash_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
-               const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+int flash_impl(const qsa_shape* s, const qsa_f16* q, const int8_t* kq, const qsa_f16* ksc,
+               const int8_t* vq, const qsa_f16* vsc, const int32_t* ids, qsa_f16* out,
                float* part, void* workspace, int64_t workspace_bytes, void* stream,
                int64_t need) {
   qsa::RowArgs a;
@@ -292,17 +292,17 @@ int flash_impl(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _F
 
 extern "C" {
 
-int qsa_flash_prepare(const qsa_shape* s, const int8_t* kq, const _Float16* ksc,
-                      const int8_t* vq, const _Float16* vsc, void* workspace,
+int qsa_flash_prepare(const qsa_shape* s, const int8_t* kq, const qsa_f16* ksc,
+                      const int8_t* vq, const qsa_f16* vsc, void* workspace,
                       int64_t workspace_bytes, void* stream) {
   const int rc = check_shape(s);
   if (rc != QSA_OK) return rc;
   return prepare_impl(s, kq, ksc, vq, vsc, workspace, workspace_bytes, stream, full_workspace(s));
 }
 
-int qsa_flash_attend(const qsa_shape* s, const _Float16* q, const int8_t* kq,
-                     const _Float16* ksc, const int8_t* vq, const _Float16* vsc,
-                     const int32_t* ids, _Float16* out, void* workspace, int64_t workspace_bytes,
+int qsa_flash_attend(const qsa_shape* s, const qsa_f16* q, const int8_t* kq,
+                     const qsa_f16* ksc, const int8_t* vq, const qsa_f16* vsc,
+                     const int32_t* ids, qsa_f16* out, void* workspace, int64_t workspace_bytes,
                      void* stream) {
   const int rc = check_shape(s);
   if (rc != QSA_OK) return rc;
@@ -310,8 +310,8 @@ int qsa_flash_attend(const qsa_shape* s, const _Float16* q, const int8_t* kq,
                      full_workspace(s));
 }
 
-int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Float16* ksc,
-              const int8_t* vq, const _Float16* vsc, const int32_t* ids, _Float16* out,
+int qsa_flash(const qsa_shape* s, const qsa_f16* q, const int8_t* kq, const qsa_f16* ksc,
+              const int8_t* vq, const qsa_f16* vsc, const int32_t* ids, qsa_f16* out,
               float* part, void* workspace, int64_t workspace_bytes, void* stream) {
   const int rc = check_shape(s);
   if (rc != QSA_OK) return rc;
@@ -319,23 +319,26 @@ int qsa_flash(const qsa_shape* s, const _Float16* q, const int8_t* kq, const _Fl
                     part ? 0 : full_workspace(s));
 }
 
-int qsa_merge(const qsa_shape* s, const float* part, _Float16* out, void* stream) {
+int qsa_merge(const qsa_shape* s, const float* part, qsa_f16* out, void* stream) {
   int rc = check_shape(s);
   if (rc != QSA_OK) return rc;
   if (!part || !out || !aligned(part, 16) || !aligned(out, 16)) return QSA_ERR_ARG;
-  return launch_status(qsa::launch_merge(part, out, s->T, s->n_groups * QSA_HEADS_PER_GROUP,
+  return launch_status(qsa::launch_merge(part, reinterpret_cast<_Float16*>(out), s->T,
+                                         s->n_groups * QSA_HEADS_PER_GROUP,
                                          s->pos0, s->budget, 1, (hipStream_t)stream));
 }
 
-int qsa_quantize(int64_t n_rows, int32_t dim, const _Float16* x, int8_t* codes,
-                 _Float16* scales, void* stream) {
+int qsa_quantize(int64_t n_rows, int32_t dim, const qsa_f16* x, int8_t* codes,
+                 qsa_f16* scales, void* stream) {
   if (dim != QSA_HEAD_DIM) return QSA_ERR_UNSUPPORTED;
   // one workgroup per 16 rows on a 1-D grid
   if (n_rows < 0 || n_rows > (int64_t)INT32_MAX * 16) return QSA_ERR_SHAPE;
   if (n_rows == 0) return QSA_OK;
   if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2))
     return QSA_ERR_ARG;
-  return launch_status(qsa::launch_quantize(x, codes, scales, n_rows, (hipStream_t)stream));
+  return launch_status(qsa::launch_quantize(reinterpret_cast<const _Float16*>(x), codes,
+                                            reinterpret_cast<_Float16*>(scales), n_rows,
+                                            (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -364,9 +367,9 @@ void* scratch_ptr() {
 
 extern "C" {
 
-int qsa_flash_noalloc(const qsa_shape* s, const _Float16* q, const int8_t* kq,
-                      const _Float16* ksc, const int8_t* vq, const _Float16* vsc,
-                      const int32_t* ids, _Float16* out, float* part, void* stream) {
+int qsa_flash_noalloc(const qsa_shape* s, const qsa_f16* q, const int8_t* kq,
+                      const qsa_f16* ksc, const int8_t* vq, const qsa_f16* vsc,
+                      const int32_t* ids, qsa_f16* out, float* part, void* stream) {
   // every host-side check of qsa_flash first (nothing touches the device)
   qsa::RowArgs a;
   int rc = flash_args(s, q, kq, ksc, vq, vsc, ids, out, part, &a);

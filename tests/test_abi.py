@@ -5,6 +5,7 @@ import ctypes
 import json
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -257,3 +258,46 @@ def test_noalloc_checks_arguments_and_scratch_size_on_the_host():
     assert qsa.qsa_flash_workspace_bytes(fit) == qsa.NOALLOC_SCRATCH_BYTES + 256 + 3 * 2 * slot
     assert qsa.qsa_status_string(qsa.QSA_ERR_TOO_LARGE) != "unknown status"
     assert qsa.qsa_status_string(qsa.QSA_ERR_DEVICE) != "unknown status"
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "qsa.h"
+int main(void) {
+  qsa_shape s = {96, 2050, 2, QSA_HEADS_PER_GROUP, QSA_HEAD_DIM, QSA_DEFAULT_BUDGET, 2146};
+  qsa_shape bad = s;
+  bad.T = 0;
+  const qsa_f16 *q = 0;
+  qsa_f16 *out = 0;
+  printf("%lld %lld\n", (long long)qsa_flash_workspace_bytes(&s), (long long)qsa_part_elems(&s));
+  printf("%d %d\n", qsa_flash(&s, q, 0, 0, 0, 0, 0, out, 0, 0, 0, 0),
+         qsa_flash(&bad, q, 0, 0, 0, 0, 0, out, 0, 0, 0, 0));
+  printf("%d %d\n", qsa_quantize(3, 128, 0, 0, 0, 0), qsa_merge(&s, 0, out, 0));
+  printf("%s\n", qsa_status_string(QSA_ERR_SHAPE));
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # a C11 program (gcc, pedantic, warnings as errors) and the same source
+    # as C++17 include the header; the C one links libqsa.so and calls it
+    # (argument checks only: nothing reaches the GPU)
+    lib = qsa.load_library()
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    inc = os.path.join(ROOT, "include")
+    libdir = os.path.dirname(qsa.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc,
+                    str(src), "-L", libdir, "-lqsa", "-Wl,-rpath," + libdir, "-o", str(exe)],
+                   check=True)
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-pedantic", "-Werror", "-x", "c++",
+                    "-I", inc, "-c", str(src), "-o", str(tmp_path / "abi_cpp.o")], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, check=True, timeout=60)
+    lines = r.stdout.splitlines()
+    s = qsa.QsaShape(T=96, pos0=2050, n_groups=2, n_cells=2146)
+    assert lines[0] == "%d %d" % (qsa.qsa_flash_workspace_bytes(s), qsa.qsa_part_elems(s))
+    assert lines[1] == "%d %d" % (qsa.QSA_ERR_ARG, qsa.QSA_ERR_SHAPE)
+    assert lines[2] == "%d %d" % (qsa.QSA_ERR_UNSUPPORTED, qsa.QSA_ERR_ARG)
+    assert lines[3] == lib.qsa_status_string(qsa.QSA_ERR_SHAPE).decode()
