@@ -1,5 +1,8 @@
 """Seeded random shapes through the selection, fused, no-alloc and split +
-merge paths, against the oracle.  T, pos0, budget, the number of KV groups
+merge paths, against the oracle: 64 draws with 1-3 KV groups and budgets
+up to 2051, and 32 wider ones with up to 8 groups and budgets up to 8192
+(where the identity prefix's images exceed the no-alloc scratch, that call
+must refuse with QSA_ERR_TOO_LARGE).  T, pos0, budget, the number of KV groups
 and spare history cells are drawn so that the calls take every route
 (tiled blocks with and without split pieces, every token split, split rows
 after tiled tokens, the row kernel) and meet ragged chunk, block and budget
@@ -51,7 +54,29 @@ def _check(got, ref, what):
     assert worst_row_rel_l2(got, ref) <= 4e-3, what
 
 
-@pytest.mark.parametrize("case,T,pos0,budget,G,spare", _cases())
+def _wide_cases(n=32, seed=101):
+    """Wider draws: up to 8 KV groups, budgets from 1 to 8192 (identity
+    prefixes up to 128 chunks), chunks up to 699 tokens."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        G = int(rng.choice([1, 2, 4, 5, 8]))
+        budget = int(rng.choice([1, 63, 64, 129, 777, 2051, 4096, 8192]))
+        T = int(rng.integers(1, 700))
+        kind = int(rng.integers(0, 3))
+        if kind == 0:
+            pos0 = int(rng.integers(0, max(1, budget - T + 1)))
+        elif kind == 1:
+            pos0 = max(0, budget - int(rng.integers(1, T + 1)))
+        else:
+            pos0 = budget + int(rng.integers(0, 5000))
+        spare = int(rng.choice([0, 5, 1000]))
+        if _visits(T, pos0, budget, G) <= 1_500_000:
+            out.append((1000 + len(out), T, pos0, budget, G, spare))
+    return out
+
+
+@pytest.mark.parametrize("case,T,pos0,budget,G,spare", _cases() + _wide_cases())
 def test_random_shape(case, T, pos0, budget, G, spare):
     inp = qsa_synth.layer_inputs(T, pos0, layer=case, seed=77, budget=budget,
                                  n_cells=pos0 + T + spare, n_groups=G)
@@ -66,7 +91,15 @@ def test_random_shape(case, T, pos0, budget, G, spare):
     s = shape_of(inp)
     idt = None if ids is None else torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
     out = Guarded((s.T, s.n_heads, s.head_dim), torch.float16, fill=float("nan"))
-    qsa.qsa_flash_noalloc(s, dev["q"], dev["kq"], dev["ksc"], dev["vq"], dev["vsc"], idt, out.t)
-    _check(out.numpy("qsa_flash_noalloc out").astype(np.float64), ref, "qsa_flash_noalloc")
+    images = G * -(-min(pos0 + T, budget) // qsa.CHUNK) * 65536 if pos0 < budget else 0
+    if images <= qsa.NOALLOC_SCRATCH_BYTES:
+        qsa.qsa_flash_noalloc(s, dev["q"], dev["kq"], dev["ksc"], dev["vq"], dev["vsc"], idt,
+                              out.t)
+        _check(out.numpy("qsa_flash_noalloc out").astype(np.float64), ref, "qsa_flash_noalloc")
+    else:  # the identity prefix's chunk images exceed the static scratch
+        with pytest.raises(qsa.QsaError) as e:
+            qsa.qsa_flash_noalloc(s, dev["q"], dev["kq"], dev["ksc"], dev["vq"], dev["vsc"], idt,
+                                  out.t)
+        assert e.value.status == qsa.QSA_ERR_TOO_LARGE
 
     _check(gpu_split_merge(inp, ids, dev), ref, "split + merge")
